@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of one fused prefix-shared decode step on one MI355X.
+
+A step is one launch of the fused kernel over the whole batch of the chosen
+workload (default: Llama-3-8B attention shape, 8 prefix groups x 100
+requests, 2048-token prefixes, distinct lengths U[64, 512], bf16), with Q and
+the paged K/V pools already resident in HBM.  The plan is built and uploaded
+before timing.  Each timed step is bracketed by HIP events on the launch
+stream; L2 and the 256 MB MALL are flushed (1 GiB write) before every step,
+outside the events.  Prints one JSON line.
+
+--gpus N with N > 1 is refused: this build measures one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attention queries/s + effective KV GB/s (% of HBM roofline), 8×100 groups"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "psa_internal.h", "plan.cpp"):
+        with open(os.path.join(ROOT, "prefix_shared_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, launch_bytes_alg):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this kernel."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def describe(wl, batch):
+    import numpy as np
+
+    lp = np.asarray(batch["group_prefix_len"])
+    ld = np.asarray(batch["query_distinct_len"])
+    return {
+        "workload": wl.name,
+        "num_queries": int(len(batch["query_group"])),
+        "prefix_groups": int(len(lp)),
+        "prefix_tokens": sorted(set(int(x) for x in lp))[:4],
+        "distinct_tokens_min_max_mean": [int(ld.min()), int(ld.max()), round(float(ld.mean()), 1)] if len(ld) else [],
+        "q_heads": wl.num_q_heads,
+        "kv_heads": wl.num_kv_heads,
+        "head_dim": wl.head_dim,
+        "page_size": wl.page_size,
+        "kv_dtype": wl.dtype,
+        "seed": wl.seed,
+    }
+
+
+def cpu_baseline(wl, batch, q, k, v, target_s, max_s):
+    """The fp64 oracle on a bounded sample of the same workload, queries/s."""
+    import numpy as np
+
+    import oracle
+    from workloads import subset_for_queries
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = 1
+    n = len(batch["query_group"])
+    rng = np.random.default_rng(123)
+    order = rng.permutation(n)
+
+    def run(count):
+        import torch
+
+        qs = sorted(int(x) for x in order[:count])
+        sub, page_ids = subset_for_queries(batch, qs)
+        idx = torch.as_tensor(page_ids, device=k.device, dtype=torch.long)
+        ks = k.index_select(0, idx).float().cpu().numpy()
+        vs = v.index_select(0, idx).float().cpu().numpy()
+        qh = q.index_select(0, torch.as_tensor(qs, device=q.device)).float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.decode_attention(qh, ks, vs, sub)
+        return time.perf_counter() - t0
+
+    count = 4
+    el = run(count)
+    while el < target_s / 4 and count < n:
+        count = min(n, count * 4)
+        el = run(count)
+    if el < target_s and count < n:
+        count = min(n, max(count + 1, int(count * target_s / max(el, 1e-3))))
+        el = run(count)
+    while el > max_s and count > 1:
+        count = max(1, count // 2)
+        el = run(count)
+    return {
+        "value": count / el,
+        "unit": "queries/s",
+        "cores": int(threads),
+        "host_cpus": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"{count} of {n} queries of {wl.name} (all heads), fp64 numpy oracle, {el:.1f} s",
+        "note": "plain fp64 oracle on the host cores: a reported baseline, not the target",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_8x100")
+    ap.add_argument("--no-flush", action="store_true", help="do not flush L2/MALL between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--flags", type=int, default=0, help="psa_plan flags (e.g. 1 = PREFIX_ONLY)")
+    ap.add_argument("--prefix-chunk", type=int, default=0)
+    ap.add_argument("--distinct-chunk", type=int, default=0)
+    ap.add_argument("--tile-rows", type=int, default=0)
+    ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the prefix-shared decode path shards by prefix group or kv head with no exchange, "
+              "see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import prefix_shared_decode_amd as P
+    from workloads import make_values, make_workload
+
+    torch.cuda.set_device(0)
+    wl = make_workload(args.workload)
+    batch = wl.batch
+    if wl.tree is not None:
+        t0 = time.perf_counter()
+        batch, saved = P.psa_flatten_prefix_tree(wl.tree)
+        log(f"flattened two-level tree in {1e3 * (time.perf_counter() - t0):.1f} ms (saved tokens {saved})")
+    log(f"workload {wl.name}: generating inputs on the GPU")
+    q, k, v = make_values(wl, "cuda")
+    cfg = P.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.dtype, "f32")
+    t0 = time.perf_counter()
+    plan = P.psa_build_plan(cfg, batch, flags=args.flags, prefix_chunk_tokens=args.prefix_chunk,
+                            distinct_chunk_tokens=args.distinct_chunk, mfma_tile_rows=args.tile_rows)
+    plan_ms = 1e3 * (time.perf_counter() - t0)
+    info = plan.info()
+    ws = torch.empty(max(int(info["workspace_bytes"]), 256), dtype=torch.uint8, device="cuda")
+    P.psa_plan_upload(plan, ws)
+    torch.cuda.synchronize()
+    n = len(batch["query_group"])
+    out = torch.empty((n, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    log(f"plan: {info['num_items']} items ({info['num_prefix_items']} MFMA prefix, {info['num_matvec_items']} "
+        f"mat-vec), workspace {info['workspace_bytes'] / 2**20:.1f} MiB, built in {plan_ms:.1f} ms")
+
+    def step():
+        P.psa_decode_attention(plan, q, k, v, out, ws)
+
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    times_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms = float(times_ms.mean())
+    sec = ms / 1e3
+    bytes_alg = info["algorithmic_bytes"]
+    kv_alg = info["prefix_kv_bytes"] + info["distinct_kv_bytes"]
+    achieved = bytes_alg / sec / 1e9
+    traffic = load_traffic(wl.name, bytes_alg)
+    rec = {
+        "metric": METRIC,
+        "value": n / sec,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, shuffled pages)",
+        "config": describe(wl, batch),
+        "effective_kv_GBps": kv_alg / sec / 1e9,
+        "hbm_roofline_frac": achieved / HBM_PEAK_GBPS,
+        "ms_p10_p50_p90": [float(np.percentile(times_ms, p)) for p in (10, 50, 90)],
+        "timing": "HIP events around each launch on its stream; L2+MALL flushed before each step"
+                  if flush is not None else "HIP events around each launch; caches warm",
+        "timed_region_wall_s": t_wall,
+        "plan": {"build_ms": plan_ms, "items": info["num_items"], "mfma_prefix_items": info["num_prefix_items"],
+                 "matvec_items": info["num_matvec_items"], "flags": args.flags,
+                 "saved_tokens": info["saved_tokens"], "logical_tokens": info["logical_tokens"]},
+        "roofline": {
+            "kernel": "psa::decode_kernel<128,4,true> (fused prefix MFMA + distinct mat-vec + merge)"
+            if wl.num_q_heads // wl.num_kv_heads == 4 else "psa::decode_kernel (fused)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": bytes_alg,
+            "traffic": traffic,
+        },
+    }
+    if info["prefix_flops"] > 0:
+        rec["roofline"]["prefix_flops_per_launch"] = info["prefix_flops"]
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the fp64 oracle on a sample")
+        rec["cpu_baseline"] = cpu_baseline(wl, batch, q, k, v, args.cpu_seconds, 30.0)
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * psa.h - prefix-shared decode attention on MI355X (gfx950), C ABI.
+ *
+ * What the library computes (BatchLLM summary, papercache.org, §2.2 Eq. 1 and
+ * §5): every decode query of a prefix-sharing group attends once to the
+ * group's shared-prefix KV and once to its own distinct KV; the two partial
+ * results are merged by online softmax.  Prefix and distinct work run in ONE
+ * horizontally fused kernel launch, in different workgroups with different
+ * tilings (§5 "horizontal fusion of prefix-shared attention").  The KV cache is
+ * paged: logically contiguous tokens live in scattered fixed-size pages named
+ * by a block table (BatchLLM §2.2; continuous-batching post on guijiagi.com,
+ * "block management").  Groups are single-level (BatchLLM §5: the input is a
+ * list of (prefix, [distinct ...]) tuples); a multi-level prefix tree is first
+ * flattened by dynamic programming (BatchLLM §4.2, Fig. 4) with
+ * psa_flatten_prefix_tree.
+ *
+ * Result for query i, query head h (kv head kvh = h / (Hq/Hkv)):
+ *   context = prefix tokens of group(i) (none if group(i) == -1) ++ distinct
+ *             tokens of i;
+ *   s_t = sm_scale * <q[i,h,:], K[t]>;  m = max_t s_t;  l = sum_t exp(s_t - m);
+ *   out[i,h,:] = sum_t exp(s_t - m) V[t] / l.
+ * out_m / out_l (optional) receive m (natural-log units) and l.
+ *
+ * Conventions.
+ *   - Every function returns psa_status; nothing aborts or throws across the
+ *     ABI.  On a non-OK status psa_last_error() returns a thread-local message.
+ *   - "Device pointer" = memory allocated on the current HIP device (e.g. a
+ *     torch tensor's data_ptr()); "host pointer" = ordinary CPU memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued asynchronously; PSA_OK means "enqueued".
+ *   - The library never allocates device memory.  The caller owns every device
+ *     buffer, including the workspace.  The plan owns a pinned host staging
+ *     buffer (allocated on first upload).
+ *
+ * Tensor layouts (contiguous, row-major, base pointers 16-byte aligned):
+ *   q                [num_queries, num_q_heads, head_dim]        kv_dtype
+ *   k_pool, v_pool   [num_pages, num_kv_heads, page_size, head_dim] kv_dtype
+ *                    (token t of a segment sits in page pages[t / page_size],
+ *                     slot t % page_size; a (page, kv head) tile is contiguous)
+ *   out              [num_queries, num_q_heads, head_dim]        out_dtype
+ *   out_m, out_l     [num_queries, num_q_heads]                  float32
+ */
+#ifndef PSA_H
+#define PSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PSA_VERSION 1
+
+typedef enum {
+  PSA_OK = 0,
+  PSA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad CSR, Hq % Hkv != 0,
+                                   negative length, empty context, ... */
+  PSA_ERR_UNSUPPORTED = 2,      /* head_dim not in {64,128}, page_size != 16,
+                                   Hq/Hkv not in {1,2,4,8}, unknown dtype */
+  PSA_ERR_OUT_OF_RANGE = 3,     /* page id >= num_pages, length > pages * page_size */
+  PSA_ERR_WORKSPACE_TOO_SMALL = 4,
+  PSA_ERR_HIP = 5,              /* a HIP runtime call failed; message has its text */
+  PSA_ERR_ALLOC = 6             /* host allocation failed */
+} psa_status;
+
+typedef enum { PSA_BF16 = 0, PSA_F32 = 1 } psa_dtype;
+
+/* Model/cache shape.  sm_scale <= 0 selects 1/sqrt(head_dim) (the scale of
+ * the continuous-batching post's "attention computation" section). */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t page_size;  /* 16 */
+  int32_t num_pages;  /* pages in each of k_pool / v_pool */
+  int32_t kv_dtype;   /* psa_dtype of q, k_pool, v_pool */
+  int32_t out_dtype;  /* psa_dtype of out (PSA_F32 recommended) */
+  float sm_scale;
+} psa_config;
+
+/* Single-level prefix-sharing groups (BatchLLM §5: tuple(prefix, [distinct...]))
+ * over paged KV.  Host pointers, borrowed for the duration of the call only.
+ * CSR page tables: group g's prefix pages are
+ * group_pages[group_page_off[g] .. group_page_off[g+1]), holding
+ * group_prefix_len[g] tokens; likewise per query for its distinct part.
+ * query_group[i] = -1: query i shares no prefix.  A query whose context is
+ * empty (no prefix and distinct length 0) is rejected. */
+typedef struct {
+  int32_t num_groups;
+  const int32_t* group_prefix_len;   /* [num_groups] */
+  const int64_t* group_page_off;     /* [num_groups + 1], starts at 0, non-decreasing */
+  const int32_t* group_pages;        /* [group_page_off[num_groups]] */
+  int32_t num_queries;
+  const int32_t* query_group;        /* [num_queries], -1 or a group id */
+  const int32_t* query_distinct_len; /* [num_queries], may be 0 */
+  const int64_t* query_page_off;     /* [num_queries + 1] */
+  const int32_t* query_pages;        /* [query_page_off[num_queries]] */
+} psa_batch;
+
+/* Plan flags. */
+#define PSA_PLAN_PREFIX_ONLY 0x1u   /* cover only prefix tokens: out = prefix partial */
+#define PSA_PLAN_DISTINCT_ONLY 0x2u /* cover only distinct tokens: out = distinct partial */
+#define PSA_PLAN_FORCE_MATVEC 0x4u  /* no MFMA prefix tiles: every range per query */
+#define PSA_PLAN_DEBUG_POISON 0x8u  /* psa_plan_upload fills partial slots with NaN */
+#define PSA_PLAN_NO_XCD_ORDER 0x10u /* plain longest-first order, no XCD grouping */
+
+/* Plan options; pass NULL for defaults.  Zero fields take defaults. */
+typedef struct {
+  uint32_t flags;
+  int32_t prefix_chunk_tokens;   /* KV-range chunk of prefix work (split-K); default 2048 */
+  int32_t distinct_chunk_tokens; /* chunk of distinct work; default 512 */
+  int32_t mfma_min_rows;         /* group rows (members * Hq/Hkv) at or above which the
+                                    prefix uses the MFMA tile; default 16 */
+  int32_t mfma_tile_rows;        /* max rows per MFMA prefix tile, multiple of 16, <= 128;
+                                    default 128 */
+} psa_plan_opts;
+
+/* Plan statistics (host side). */
+typedef struct {
+  size_t workspace_bytes;    /* device workspace psa_plan_upload/psa_decode_attention need */
+  int64_t num_items;         /* workgroups of the fused launch */
+  int64_t num_prefix_items;  /* MFMA prefix tiles */
+  int64_t num_matvec_items;  /* mat-vec tiles (distinct ranges, small-group prefixes) */
+  int64_t num_partial_slots; /* (query, kv head) partial results written to the workspace */
+  int64_t logical_tokens;    /* sum over queries of attended tokens */
+  int64_t processed_tokens;  /* prefix tokens once per group + distinct tokens */
+  int64_t saved_tokens;      /* logical - processed (BatchLLM §3.2 Eq. 2 numerator) */
+  double algorithmic_bytes;  /* KV read once per group/query + q + out (fp32 or bf16) */
+  double algorithmic_flops;  /* 4 * head_dim * Hq per attended token */
+  double prefix_flops;       /* part of algorithmic_flops on prefix tokens */
+  double prefix_kv_bytes;    /* prefix KV bytes, once per group */
+  double distinct_kv_bytes;  /* distinct KV bytes */
+} psa_plan_info;
+
+typedef struct psa_plan psa_plan;
+
+/* Validate `batch` against `cfg`, split every KV range into chunks, classify
+ * them into MFMA prefix tiles and mat-vec tiles, order the work list (longest
+ * first, tiles sharing a prefix chunk on the same XCD) and lay out the
+ * workspace.  Host only; copies everything it needs.  *out receives a new plan
+ * on PSA_OK (free with psa_destroy_plan). */
+psa_status psa_build_plan(const psa_config* cfg, const psa_batch* batch,
+                          const psa_plan_opts* opts, psa_plan** out);
+
+psa_status psa_plan_get_info(const psa_plan* plan, psa_plan_info* info);
+
+/* Copy the plan's work list and page tables into the device workspace
+ * `d_workspace` (>= info.workspace_bytes) on `stream`, and zero its merge
+ * counters.  Needed once per (plan, workspace) pair; afterwards the workspace
+ * serves any number of psa_decode_attention calls of this plan (counters
+ * reset themselves).  The plan must stay alive until the copy has completed
+ * (synchronise the stream before psa_destroy_plan). */
+psa_status psa_plan_upload(psa_plan* plan, void* d_workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* One fused launch of the decode step described by `plan` (BatchLLM §5).
+ * d_q / d_k_pool / d_v_pool / d_out: device pointers, layouts above.
+ * d_out_m, d_out_l: device pointers or NULL.  d_workspace: the workspace
+ * uploaded for this plan.  Concurrent calls on one workspace race (the merge
+ * counters live there); use one workspace per stream. */
+psa_status psa_decode_attention(const psa_plan* plan, const void* d_q, const void* d_k_pool,
+                                const void* d_v_pool, void* d_out, float* d_out_m,
+                                float* d_out_l, void* d_workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Eq. 1's online_softmax merge of two partial results, elementwise over `rows`
+ * rows of `head_dim` (a power of two in [4, 256]):
+ *   m = max(m_a, m_b); w_x = l_x * exp(m_x - m); l = w_a + w_b;
+ *   o = (w_a o_a + w_b o_b) / l.
+ * Partials carry o normalised by their own l, m in natural-log units; the
+ * empty partial (o = 0, m = -inf, l = 0) is the identity.  All device
+ * pointers, fp32 (o_a, o_b, o 16-byte aligned); outputs may alias the `a`
+ * inputs.  PSA_ERR_UNSUPPORTED for another head_dim. */
+psa_status psa_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* m_a,
+                     const float* l_a, const float* o_b, const float* m_b, const float* l_b,
+                     float* o, float* m, float* l, void* stream);
+
+/* Multi-level input: a compact prefix tree over page-aligned KV segments
+ * (BatchLLM §4.2, Fig. 4).  Node d holds node_len[d] tokens in pages
+ * node_pages[node_page_off[d] .. node_page_off[d+1]); node_parent[d] = -1 for
+ * a child of the (empty) root.  Query i shares the whole path root..query_node[i]
+ * (-1 = nothing) and owns query_distinct_len[i] further tokens.  Host pointers. */
+typedef struct {
+  int32_t num_nodes;
+  const int32_t* node_parent;   /* [num_nodes], parent id < own id not required */
+  const int32_t* node_len;      /* [num_nodes], multiple of page_size, > 0 */
+  const int64_t* node_page_off; /* [num_nodes + 1] */
+  const int32_t* node_pages;
+  int32_t num_queries;
+  const int32_t* query_node;         /* [num_queries] */
+  const int32_t* query_distinct_len; /* [num_queries] */
+  const int64_t* query_page_off;     /* [num_queries + 1] */
+  const int32_t* query_pages;
+} psa_tree;
+
+typedef struct psa_batch_owned psa_batch_owned;
+
+/* Flatten `tree` to single-level groups maximising first-level token reuse,
+ * sum over groups of prefix_len * (members - 1) (BatchLLM §4.2).  Each group is
+ * a tree node's root-to-node path; nodes below it are unfolded into the
+ * members' distinct parts.  Groups are numbered by node id, queries keep their
+ * order.  *out receives a library-owned batch (free with psa_free_batch). */
+psa_status psa_flatten_prefix_tree(const psa_tree* tree, int32_t page_size,
+                                   psa_batch_owned** out);
+
+/* View of a flattened batch (pointers stay valid until psa_free_batch) and
+ * the saved-token count of its grouping. */
+psa_status psa_batch_owned_view(const psa_batch_owned* owned, psa_batch* view,
+                                int64_t* saved_tokens);
+
+void psa_free_batch(psa_batch_owned* owned);
+void psa_destroy_plan(psa_plan* plan);
+
+/* Thread-local text of the last non-OK status ("" if none). */
+const char* psa_last_error(void);
+
+int32_t psa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSA_H */

@@ -1,0 +1,30 @@
+"""Prefix-shared decode attention for MI355X (gfx950): Python binding of libpsa.so.
+
+The entry points keep the C names (include/psa.h): ``psa_build_plan``,
+``psa_plan_upload``, ``psa_decode_attention``, ``psa_merge``,
+``psa_flatten_prefix_tree``, ``psa_plan_get_info``.  The library is loaded on
+first use and its absence is an error.
+"""
+
+from ._lib import (  # noqa: F401
+    DEBUG_POISON,
+    DISTINCT_ONLY,
+    EXPORTS,
+    FORCE_MATVEC,
+    LIB_PATH,
+    NO_XCD_ORDER,
+    PREFIX_ONLY,
+    PSA_BF16,
+    PSA_F32,
+    Plan,
+    PsaError,
+    lib,
+    make_config,
+    psa_build_plan,
+    psa_decode_attention,
+    psa_flatten_prefix_tree,
+    psa_merge,
+    psa_plan_get_info,
+    psa_plan_upload,
+)
+from .runner import DecodeStep  # noqa: F401

@@ -1,0 +1,270 @@
+// C ABI of the prefix-shared decode attention library (declared in psa.h).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "plan.h"
+#include "psa_internal.h"
+
+namespace psa {
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int r, bool bf16, hipStream_t s);
+hipError_t launch_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* m_a, const float* l_a,
+                        const float* o_b, const float* m_b, const float* l_b, float* o, float* m, float* l,
+                        hipStream_t s);
+hipError_t launch_fill(uint32_t* dst, int64_t n, uint32_t value, hipStream_t s);
+
+namespace {
+thread_local std::string g_err;
+
+psa_status hip_fail(hipError_t e, const char* what) {
+  return set_error(PSA_ERR_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")");
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A device pointer of the current device (or managed memory); host pointers
+// and pointers of another device are rejected before any kernel sees them.
+psa_status check_device_ptr(const void* ptr, const char* name, int device) {
+  if (!ptr) return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(name) + " is NULL");
+  if (!aligned16(ptr)) return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(name) + " is not 16-byte aligned");
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(name) + " is not device memory");
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(name) + " is not device memory");
+  if (attr.device != device)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(name) + " lives on another device");
+  return PSA_OK;
+}
+}  // namespace
+
+psa_status set_error(psa_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+}  // namespace psa
+
+using psa::set_error;
+
+extern "C" {
+
+const char* psa_last_error(void) { return psa::g_err.c_str(); }
+
+int32_t psa_version(void) { return PSA_VERSION; }
+
+psa_status psa_build_plan(const psa_config* cfg, const psa_batch* batch, const psa_plan_opts* opts,
+                          psa_plan** out) {
+  try {
+    return psa::build_plan(cfg, batch, opts, out);
+  } catch (const std::bad_alloc&) {
+    return set_error(PSA_ERR_ALLOC, "out of host memory");
+  } catch (...) {
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "unexpected exception while planning");
+  }
+}
+
+psa_status psa_plan_get_info(const psa_plan* plan, psa_plan_info* info) {
+  if (!plan || !info) return set_error(PSA_ERR_INVALID_ARGUMENT, "plan or info is NULL");
+  *info = plan->info;
+  return PSA_OK;
+}
+
+psa_status psa_plan_upload(psa_plan* plan, void* d_workspace, size_t bytes, void* stream) {
+  if (!plan) return set_error(PSA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (bytes < (size_t)plan->layout.total_bytes)
+    return set_error(PSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(plan->layout.total_bytes) +
+                                                      " bytes, got " + std::to_string(bytes));
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return psa::hip_fail(e, "hipGetDevice");
+  psa_status s = psa::check_device_ptr(d_workspace, "workspace", dev);
+  if (s != PSA_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const size_t meta = (size_t)plan->layout.meta_bytes;
+  {
+    std::lock_guard<std::mutex> lk(plan->mu);
+    if (!plan->pinned && meta > 0) {
+      e = hipHostMalloc(&plan->pinned, meta, hipHostMallocDefault);
+      if (e != hipSuccess) {
+        plan->pinned = nullptr;
+        return psa::hip_fail(e, "hipHostMalloc");
+      }
+      std::memcpy(plan->pinned, plan->image.data(), meta);
+    }
+  }
+  if (meta > 0) {
+    e = hipMemcpyAsync(d_workspace, plan->pinned, meta, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return psa::hip_fail(e, "hipMemcpyAsync (plan upload)");
+  }
+  if (plan->opts.flags & PSA_PLAN_DEBUG_POISON) {
+    const int64_t words = (plan->layout.total_bytes - plan->layout.part_o) / 4;
+    e = psa::launch_fill(reinterpret_cast<uint32_t*>(static_cast<char*>(d_workspace) + plan->layout.part_o), words,
+                         0x7fc00000u /* quiet NaN */, st);
+    if (e != hipSuccess) return psa::hip_fail(e, "poison fill launch");
+  }
+  std::lock_guard<std::mutex> lk(plan->mu);
+  const auto key = std::make_pair(reinterpret_cast<uintptr_t>(d_workspace), dev);
+  bool found = false;
+  for (auto& u : plan->uploaded) found = found || u == key;
+  if (!found) plan->uploaded.push_back(key);
+  return PSA_OK;
+}
+
+psa_status psa_decode_attention(const psa_plan* plan, const void* d_q, const void* d_k_pool, const void* d_v_pool,
+                                void* d_out, float* d_out_m, float* d_out_l, void* d_workspace, size_t bytes,
+                                void* stream) {
+  if (!plan) return set_error(PSA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  const psa::ImageLayout& L = plan->layout;
+  if (bytes < (size_t)L.total_bytes)
+    return set_error(PSA_ERR_WORKSPACE_TOO_SMALL,
+                     "workspace needs " + std::to_string(L.total_bytes) + " bytes, got " + std::to_string(bytes));
+  auto* mp = const_cast<psa_plan*>(plan);
+  auto uploaded_on = [&](int device, bool any_device) {
+    std::lock_guard<std::mutex> lk(mp->mu);
+    for (auto& u : mp->uploaded)
+      if (u.first == reinterpret_cast<uintptr_t>(d_workspace) && (any_device || u.second == device)) return true;
+    return false;
+  };
+  if (!uploaded_on(0, true))
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "workspace was not uploaded for this plan (call psa_plan_upload)");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return psa::hip_fail(e, "hipGetDevice");
+  if (!uploaded_on(dev, false))
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "workspace was uploaded on another device");
+  if (plan->items.empty()) return PSA_OK;
+  psa_status s;
+  if ((s = psa::check_device_ptr(d_q, "q", dev)) != PSA_OK) return s;
+  if ((s = psa::check_device_ptr(d_k_pool, "k_pool", dev)) != PSA_OK) return s;
+  if ((s = psa::check_device_ptr(d_v_pool, "v_pool", dev)) != PSA_OK) return s;
+  if ((s = psa::check_device_ptr(d_out, "out", dev)) != PSA_OK) return s;
+  if (d_out_m && (s = psa::check_device_ptr(d_out_m, "out_m", dev)) != PSA_OK) return s;
+  if (d_out_l && (s = psa::check_device_ptr(d_out_l, "out_l", dev)) != PSA_OK) return s;
+
+  char* ws = static_cast<char*>(d_workspace);
+  psa::DecodeParams p{};
+  p.q = d_q;
+  p.k = d_k_pool;
+  p.v = d_v_pool;
+  p.out = d_out;
+  p.out_m = d_out_m;
+  p.out_l = d_out_l;
+  p.items = reinterpret_cast<const psa::WorkItem*>(ws + L.items);
+  p.group_page_off = reinterpret_cast<const int32_t*>(ws + L.group_page_off);
+  p.group_pages = reinterpret_cast<const int32_t*>(ws + L.group_pages);
+  p.group_len = reinterpret_cast<const int32_t*>(ws + L.group_len);
+  p.member_off = reinterpret_cast<const int32_t*>(ws + L.member_off);
+  p.members = reinterpret_cast<const int32_t*>(ws + L.members);
+  p.query_page_off = reinterpret_cast<const int32_t*>(ws + L.query_page_off);
+  p.query_pages = reinterpret_cast<const int32_t*>(ws + L.query_pages);
+  p.query_group = reinterpret_cast<const int32_t*>(ws + L.query_group);
+  p.query_dlen = reinterpret_cast<const int32_t*>(ws + L.query_dlen);
+  p.expected = reinterpret_cast<const int32_t*>(ws + L.expected);
+  p.slot_off = reinterpret_cast<const int32_t*>(ws + L.slot_off);
+  p.counters = reinterpret_cast<int32_t*>(ws + L.counters);
+  p.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+  p.num_items = (int32_t)plan->items.size();
+  p.num_queries = (int32_t)plan->expected.size();
+  p.hq = plan->cfg.num_q_heads;
+  p.hkv = plan->cfg.num_kv_heads;
+  p.scale_log2 = plan->sm_scale * 1.4426950408889634f;
+  p.out_bf16 = plan->cfg.out_dtype == PSA_BF16;
+  e = psa::launch_decode(p, plan->cfg.head_dim, plan->r, plan->cfg.kv_dtype == PSA_BF16,
+                         reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return psa::hip_fail(e, "decode kernel launch");
+  return PSA_OK;
+}
+
+psa_status psa_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* m_a, const float* l_a,
+                     const float* o_b, const float* m_b, const float* l_b, float* o, float* m, float* l,
+                     void* stream) {
+  if (rows < 0) return set_error(PSA_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+  if (head_dim < 4 || head_dim > 256 || (head_dim & (head_dim - 1)))
+    return set_error(PSA_ERR_UNSUPPORTED, "psa_merge: head_dim must be a power of two in [4, 256]");
+  if (rows == 0) return PSA_OK;
+  const void* ptrs[] = {o_a, m_a, l_a, o_b, m_b, l_b, o, m, l};
+  const char* names[] = {"o_a", "m_a", "l_a", "o_b", "m_b", "l_b", "o", "m", "l"};
+  for (int t = 0; t < 9; ++t)
+    if (!ptrs[t]) return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(names[t]) + " is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return psa::hip_fail(e, "hipGetDevice");
+  for (int t = 0; t < 9; ++t) {
+    if (t == 0 || t == 3 || t == 6) {
+      psa_status s = psa::check_device_ptr(ptrs[t], names[t], dev);
+      if (s != PSA_OK) return s;
+    } else {
+      if (reinterpret_cast<uintptr_t>(ptrs[t]) & 3u)
+        return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(names[t]) + " is not 4-byte aligned");
+      hipPointerAttribute_t attr;
+      if (hipPointerGetAttributes(&attr, ptrs[t]) != hipSuccess ||
+          (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) || attr.device != dev) {
+        (void)hipGetLastError();
+        return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(names[t]) + " is not device memory of this device");
+      }
+    }
+  }
+  e = psa::launch_merge(rows, head_dim, o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return psa::hip_fail(e, "merge kernel launch");
+  return PSA_OK;
+}
+
+psa_status psa_flatten_prefix_tree(const psa_tree* tree, int32_t page_size, psa_batch_owned** out) {
+  try {
+    return psa::flatten_tree(tree, page_size, out);
+  } catch (const std::bad_alloc&) {
+    return set_error(PSA_ERR_ALLOC, "out of host memory");
+  }
+}
+
+psa_status psa_batch_owned_view(const psa_batch_owned* o, psa_batch* v, int64_t* saved_tokens) {
+  if (!o || !v) return set_error(PSA_ERR_INVALID_ARGUMENT, "owned batch or view is NULL");
+  v->num_groups = (int32_t)o->group_prefix_len.size();
+  v->group_prefix_len = o->group_prefix_len.data();
+  v->group_page_off = o->group_page_off.data();
+  v->group_pages = o->group_pages.data();
+  v->num_queries = (int32_t)o->query_group.size();
+  v->query_group = o->query_group.data();
+  v->query_distinct_len = o->query_distinct_len.data();
+  v->query_page_off = o->query_page_off.data();
+  v->query_pages = o->query_pages.data();
+  if (saved_tokens) *saved_tokens = o->saved_tokens;
+  return PSA_OK;
+}
+
+void psa_free_batch(psa_batch_owned* o) { delete o; }
+
+void psa_destroy_plan(psa_plan* plan) {
+  if (!plan) return;
+  if (plan->pinned) (void)hipHostFree(plan->pinned);
+  delete plan;
+}
+
+// ---- debug helpers (psa_debug.h): expose the host copy of a plan ----
+psa_status psa_plan_debug_items(const psa_plan* plan, int32_t* out, int64_t capacity_items) {
+  if (!plan || (!out && capacity_items > 0)) return set_error(PSA_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (capacity_items < (int64_t)plan->items.size())
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "capacity too small");
+  std::memcpy(out, plan->items.data(), plan->items.size() * sizeof(psa::WorkItem));
+  return PSA_OK;
+}
+
+psa_status psa_plan_debug_queries(const psa_plan* plan, int32_t* expected, int32_t* slot_off, int64_t capacity) {
+  if (!plan) return set_error(PSA_ERR_INVALID_ARGUMENT, "NULL plan");
+  if (capacity < (int64_t)plan->expected.size()) return set_error(PSA_ERR_INVALID_ARGUMENT, "capacity too small");
+  if (!plan->expected.empty() && (!expected || !slot_off)) return set_error(PSA_ERR_INVALID_ARGUMENT, "NULL output");
+  std::memcpy(expected, plan->expected.data(), plan->expected.size() * 4);
+  std::memcpy(slot_off, plan->slot_off.data(), plan->slot_off.size() * 4);
+  return PSA_OK;
+}
+
+}  // extern "C"

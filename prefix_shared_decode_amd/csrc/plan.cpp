@@ -1,0 +1,376 @@
+// Host plan: validate -> chunk -> classify -> order -> lay out the workspace.
+//
+// BatchLLM summary (papercache.org):
+//  * §4.3.1 / §5: the prefix-sharing group is the unit of work; the input is a
+//    list of (prefix, [distinct ...]) groups.
+//  * §5 "horizontal fusion": prefix and distinct work run in different
+//    workgroups of ONE launch, each part with its own tiling.
+//  * §2.2: the shared-prefix part becomes a matrix multiply (all queries of a
+//    group against one K/V); the distinct part stays a mat-vec.
+//  * §6.3.3: when many requests share a prefix much longer than their
+//    distinct parts, split the long KV range (split-K) so the work balances.
+//  * §3.2 Eq. 2: saved tokens = logical - processed.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "plan.h"
+
+namespace psa {
+namespace {
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t x, int64_t a) { return (x + a - 1) / a; }
+
+psa_status check_segment(const char* what, int64_t idx, int64_t len, int64_t off_a, int64_t off_b,
+                         const int32_t* pages, int32_t P, int32_t num_pages) {
+  if (len < 0)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(what) + " " + std::to_string(idx) + ": negative length");
+  if (off_b < off_a)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, std::string(what) + " page offsets not monotone at " + std::to_string(idx));
+  if (len > (off_b - off_a) * P)
+    return set_error(PSA_ERR_OUT_OF_RANGE, std::string(what) + " " + std::to_string(idx) +
+                                               ": length exceeds its pages * page_size");
+  const int64_t need = ceil_div(len, P);
+  for (int64_t t = off_a; t < off_a + need; ++t) {
+    if (pages[t] < 0 || pages[t] >= num_pages)
+      return set_error(PSA_ERR_OUT_OF_RANGE, std::string(what) + " " + std::to_string(idx) + ": page id " +
+                                                 std::to_string(pages[t]) + " outside [0, num_pages)");
+  }
+  return PSA_OK;
+}
+
+}  // namespace
+
+psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_opts* opts_in,
+                      psa_plan** out) {
+  if (!out) return set_error(PSA_ERR_INVALID_ARGUMENT, "build_plan: out is NULL");
+  *out = nullptr;
+  if (!cfg || !b) return set_error(PSA_ERR_INVALID_ARGUMENT, "build_plan: cfg or batch is NULL");
+  const psa_config c = *cfg;
+  if (c.num_q_heads <= 0 || c.num_kv_heads <= 0)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "head counts must be positive");
+  if (c.num_q_heads % c.num_kv_heads)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "num_q_heads must be a multiple of num_kv_heads");
+  const int r = c.num_q_heads / c.num_kv_heads;
+  if (r != 1 && r != 2 && r != 4 && r != 8)
+    return set_error(PSA_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads must be 1, 2, 4 or 8");
+  if (c.head_dim != 64 && c.head_dim != 128) return set_error(PSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c.page_size != 16) return set_error(PSA_ERR_UNSUPPORTED, "page_size must be 16");
+  if (c.num_pages <= 0) return set_error(PSA_ERR_INVALID_ARGUMENT, "num_pages must be positive");
+  if ((c.kv_dtype != PSA_BF16 && c.kv_dtype != PSA_F32) || (c.out_dtype != PSA_BF16 && c.out_dtype != PSA_F32))
+    return set_error(PSA_ERR_UNSUPPORTED, "dtypes must be PSA_BF16 or PSA_F32");
+  if (!(std::isfinite(c.sm_scale))) return set_error(PSA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+
+  psa_plan_opts o{};
+  if (opts_in) o = *opts_in;
+  const uint32_t known = PSA_PLAN_PREFIX_ONLY | PSA_PLAN_DISTINCT_ONLY | PSA_PLAN_FORCE_MATVEC |
+                         PSA_PLAN_DEBUG_POISON | PSA_PLAN_NO_XCD_ORDER;
+  if (o.flags & ~known) return set_error(PSA_ERR_INVALID_ARGUMENT, "unknown plan flag");
+  if ((o.flags & PSA_PLAN_PREFIX_ONLY) && (o.flags & PSA_PLAN_DISTINCT_ONLY))
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "PREFIX_ONLY and DISTINCT_ONLY are exclusive");
+  if (o.prefix_chunk_tokens == 0) o.prefix_chunk_tokens = 2048;
+  if (o.distinct_chunk_tokens == 0) o.distinct_chunk_tokens = 512;
+  if (o.mfma_min_rows == 0) o.mfma_min_rows = 16;
+  if (o.mfma_tile_rows == 0) o.mfma_tile_rows = 128;
+  if (o.prefix_chunk_tokens < 0 || o.prefix_chunk_tokens % c.page_size || o.distinct_chunk_tokens < 0 ||
+      o.distinct_chunk_tokens % c.page_size)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "chunk sizes must be positive multiples of page_size");
+  if (o.mfma_min_rows < 0) return set_error(PSA_ERR_INVALID_ARGUMENT, "mfma_min_rows must be >= 0");
+  if (o.mfma_tile_rows < 16 || o.mfma_tile_rows > 128 || o.mfma_tile_rows % 16)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "mfma_tile_rows must be a multiple of 16 in [16, 128]");
+  const bool use_prefix = !(o.flags & PSA_PLAN_DISTINCT_ONLY);
+  const bool use_distinct = !(o.flags & PSA_PLAN_PREFIX_ONLY);
+  const bool restricted = (o.flags & (PSA_PLAN_PREFIX_ONLY | PSA_PLAN_DISTINCT_ONLY)) != 0;
+
+  const int G = b->num_groups, N = b->num_queries;
+  if (G < 0 || N < 0) return set_error(PSA_ERR_INVALID_ARGUMENT, "negative group or query count");
+  if (G > 0 && (!b->group_prefix_len || !b->group_page_off))
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "group arrays are NULL");
+  if (N > 0 && (!b->query_group || !b->query_distinct_len || !b->query_page_off))
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "query arrays are NULL");
+  if (G > 0 && b->group_page_off[0] != 0) return set_error(PSA_ERR_INVALID_ARGUMENT, "group_page_off[0] != 0");
+  if (N > 0 && b->query_page_off[0] != 0) return set_error(PSA_ERR_INVALID_ARGUMENT, "query_page_off[0] != 0");
+  const int64_t n_gpages = G > 0 ? b->group_page_off[G] : 0;
+  const int64_t n_qpages = N > 0 ? b->query_page_off[N] : 0;
+  if (n_gpages > 0 && !b->group_pages) return set_error(PSA_ERR_INVALID_ARGUMENT, "group_pages is NULL");
+  if (n_qpages > 0 && !b->query_pages) return set_error(PSA_ERR_INVALID_ARGUMENT, "query_pages is NULL");
+  if (n_gpages > INT32_MAX || n_qpages > INT32_MAX)
+    return set_error(PSA_ERR_UNSUPPORTED, "page tables longer than 2^31 entries");
+  for (int g = 0; g < G; ++g) {
+    psa_status s = check_segment("group", g, b->group_prefix_len[g], b->group_page_off[g], b->group_page_off[g + 1],
+                                 b->group_pages, c.page_size, c.num_pages);
+    if (s != PSA_OK) return s;
+  }
+  for (int i = 0; i < N; ++i) {
+    const int g = b->query_group[i];
+    if (g < -1 || g >= G)
+      return set_error(PSA_ERR_INVALID_ARGUMENT, "query " + std::to_string(i) + ": group id out of range");
+    psa_status s = check_segment("query", i, b->query_distinct_len[i], b->query_page_off[i], b->query_page_off[i + 1],
+                                 b->query_pages, c.page_size, c.num_pages);
+    if (s != PSA_OK) return s;
+    const int64_t lp = g >= 0 ? b->group_prefix_len[g] : 0;
+    if (lp + b->query_distinct_len[i] == 0 && !restricted)
+      return set_error(PSA_ERR_INVALID_ARGUMENT, "query " + std::to_string(i) + ": empty context");
+  }
+
+  auto* plan = new (std::nothrow) psa_plan();
+  if (!plan) return set_error(PSA_ERR_ALLOC, "out of memory");
+  plan->cfg = c;
+  plan->opts = o;
+  plan->r = r;
+  plan->sm_scale = c.sm_scale > 0 ? c.sm_scale : 1.0f / std::sqrt((float)c.head_dim);
+  const int hkv = c.num_kv_heads, d = c.head_dim, P = c.page_size;
+  const bool bf16 = c.kv_dtype == PSA_BF16;
+  const int e = bf16 ? 2 : 4;
+
+  // members of each group, in query order (rows of the MFMA tile)
+  std::vector<int32_t> member_off(G + 1, 0), members;
+  for (int i = 0; i < N; ++i)
+    if (b->query_group[i] >= 0) ++member_off[b->query_group[i] + 1];
+  for (int g = 0; g < G; ++g) member_off[g + 1] += member_off[g];
+  members.resize(member_off[G]);
+  {
+    std::vector<int32_t> fill(member_off.begin(), member_off.end() - 1);
+    for (int i = 0; i < N; ++i)
+      if (b->query_group[i] >= 0) members[fill[b->query_group[i]]++] = i;
+  }
+
+  // partial counts per query: prefix chunks first, then distinct chunks
+  const int64_t Cp = o.prefix_chunk_tokens, Cd = o.distinct_chunk_tokens;
+  std::vector<int32_t> n_pc(N, 0), expected(N, 0), slot_off(N, -1);
+  int64_t slots = 0;
+  for (int i = 0; i < N; ++i) {
+    const int g = b->query_group[i];
+    const int64_t lp = g >= 0 ? b->group_prefix_len[g] : 0;
+    n_pc[i] = use_prefix ? (int32_t)ceil_div(lp, Cp) : 0;
+    const int64_t n_dc = use_distinct ? ceil_div(b->query_distinct_len[i], Cd) : 0;
+    expected[i] = n_pc[i] + (int32_t)n_dc;
+    if (expected[i] >= 2) {
+      slot_off[i] = (int32_t)slots;
+      slots += expected[i];
+    }
+  }
+  if (slots * hkv > INT32_MAX) {
+    delete plan;
+    return set_error(PSA_ERR_UNSUPPORTED, "too many partial slots");
+  }
+
+  // ---- work items with a cost estimate (arbitrary time units) ----
+  struct Cand {
+    WorkItem it;
+    double cost;
+    int64_t set;  // items of one set share a prefix chunk and go to one XCD
+  };
+  std::vector<Cand> cands;
+  const double bw_slot = 8.0e3 / 512.0;   // bytes per ns per workgroup slot (HBM share)
+  const double mfma_slot = 2.5e6 / 512.0 * 0.5;  // flop per ns per workgroup slot at half rate
+  const double fixed = 300.0;             // per-item overhead, ns
+  int64_t set_id = 0;
+  int64_t n_prefix_items = 0, n_matvec_items = 0;
+  const int64_t tile_max = o.mfma_tile_rows;
+  for (int g = 0; g < G && use_prefix; ++g) {
+    const int64_t lp = b->group_prefix_len[g];
+    const int nm = member_off[g + 1] - member_off[g];
+    if (lp == 0 || nm == 0) continue;
+    const int64_t rows = (int64_t)nm * r;
+    const bool mfma = bf16 && !(o.flags & PSA_PLAN_FORCE_MATVEC) && rows >= o.mfma_min_rows;
+    const int64_t nchunks = ceil_div(lp, Cp);
+    for (int64_t ch = 0; ch < nchunks; ++ch) {
+      const int32_t tb = (int32_t)(ch * Cp), te = (int32_t)std::min(lp, (ch + 1) * Cp);
+      const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
+      if (mfma) {
+        const int64_t ntiles = ceil_div(rows, tile_max);
+        const int64_t per = round_up(ceil_div(rows, ntiles), 16);
+        for (int kvh = 0; kvh < hkv; ++kvh) {
+          for (int64_t rb = 0; rb < rows; rb += per) {
+            const int64_t rc = std::min(per, rows - rb);
+            WorkItem it{ITEM_PREFIX_MFMA, kvh, g, tb, te, (int32_t)rb, (int32_t)rc, (int32_t)ch};
+            const double fl = (double)round_up(te - tb, 64) * round_up(rc, 16) * d * 4;
+            cands.push_back({it, fixed + std::max(fl / mfma_slot, kv_bytes / bw_slot), set_id});
+            ++n_prefix_items;
+          }
+          ++set_id;
+        }
+      } else {
+        for (int t = member_off[g]; t < member_off[g + 1]; ++t) {
+          for (int kvh = 0; kvh < hkv; ++kvh) {
+            WorkItem it{ITEM_MATVEC_PREFIX, kvh, members[t], tb, te, 0, 0, (int32_t)ch};
+            cands.push_back({it, fixed + kv_bytes / bw_slot, set_id++});
+            ++n_matvec_items;
+          }
+        }
+      }
+    }
+  }
+  for (int i = 0; i < N && use_distinct; ++i) {
+    const int64_t ld = b->query_distinct_len[i];
+    const int64_t nchunks = ceil_div(ld, Cd);
+    for (int64_t ch = 0; ch < nchunks; ++ch) {
+      const int32_t tb = (int32_t)(ch * Cd), te = (int32_t)std::min(ld, (ch + 1) * Cd);
+      const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
+      for (int kvh = 0; kvh < hkv; ++kvh) {
+        WorkItem it{ITEM_MATVEC_DISTINCT, kvh, i, tb, te, 0, 0, (int32_t)(n_pc[i] + ch)};
+        cands.push_back({it, fixed + kv_bytes / bw_slot, set_id++});
+        ++n_matvec_items;
+      }
+    }
+  }
+  for (int i = 0; i < N; ++i) {
+    if (expected[i] == 0) {  // only under PREFIX_ONLY / DISTINCT_ONLY
+      WorkItem it{ITEM_EMPTY, 0, i, 0, 0, 0, 0, 0};
+      cands.push_back({it, 1.0, set_id++});
+    }
+  }
+
+  // ---- ordering: longest first; sets spread over 8 XCD queues (workgroup
+  // i runs on XCD i % 8), so tiles re-reading one prefix chunk share an L2 ----
+  std::vector<WorkItem> items;
+  items.reserve(cands.size());
+  if (o.flags & PSA_PLAN_NO_XCD_ORDER) {
+    std::stable_sort(cands.begin(), cands.end(), [](const Cand& a, const Cand& b2) { return a.cost > b2.cost; });
+    for (auto& x : cands) items.push_back(x.it);
+  } else {
+    // group candidates by set
+    std::vector<int64_t> order(cands.size());
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b2) {
+      if (cands[a].set != cands[b2].set) return cands[a].set < cands[b2].set;
+      return a < b2;
+    });
+    struct Set {
+      int64_t begin, end;
+      double cost;
+    };
+    std::vector<Set> sets;
+    for (size_t t = 0; t < order.size();) {
+      size_t u = t;
+      double cs = 0;
+      while (u < order.size() && cands[order[u]].set == cands[order[t]].set) cs += cands[order[u++]].cost;
+      sets.push_back({(int64_t)t, (int64_t)u, cs});
+      t = u;
+    }
+    std::stable_sort(sets.begin(), sets.end(), [](const Set& a, const Set& b2) { return a.cost > b2.cost; });
+    constexpr int kXcd = 8;
+    std::vector<std::vector<int64_t>> q(kXcd);
+    double load[kXcd] = {0};
+    for (const Set& s : sets) {
+      int best = 0;
+      for (int x = 1; x < kXcd; ++x)
+        if (load[x] < load[best]) best = x;
+      for (int64_t t = s.begin; t < s.end; ++t) q[best].push_back(order[t]);
+      load[best] += s.cost;
+    }
+    for (auto& qq : q)
+      std::stable_sort(qq.begin(), qq.end(), [&](int64_t a, int64_t b2) { return cands[a].cost > cands[b2].cost; });
+    size_t longest = 0;
+    for (auto& qq : q) longest = std::max(longest, qq.size());
+    for (size_t k = 0; k < longest; ++k)
+      for (int x = 0; x < kXcd; ++x)
+        if (k < q[x].size()) items.push_back(cands[q[x][k]].it);
+  }
+  if (items.size() > (size_t)INT32_MAX) {
+    delete plan;
+    return set_error(PSA_ERR_UNSUPPORTED, "work list too long");
+  }
+
+  // ---- workspace image ----
+  ImageLayout L{};
+  int64_t off = 0;
+  auto sect = [&](int64_t bytes) {
+    int64_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.items = sect((int64_t)items.size() * (int64_t)sizeof(WorkItem));
+  L.group_page_off = sect((G + 1) * 4);
+  L.group_pages = sect(n_gpages * 4);
+  L.group_len = sect(G * 4);
+  L.member_off = sect((G + 1) * 4);
+  L.members = sect((int64_t)members.size() * 4);
+  L.query_page_off = sect((N + 1) * 4);
+  L.query_pages = sect(n_qpages * 4);
+  L.query_group = sect(N * 4);
+  L.query_dlen = sect(N * 4);
+  L.expected = sect(N * 4);
+  L.slot_off = sect(N * 4);
+  L.counters = sect((int64_t)N * hkv * 4);
+  L.meta_bytes = off;
+  L.part_o = sect(slots * hkv * r * d * 4);
+  L.part_ml = sect(slots * hkv * r * 2 * 4);
+  L.total_bytes = off;
+  plan->layout = L;
+
+  std::vector<uint8_t>& img = plan->image;
+  try {
+    img.assign((size_t)L.meta_bytes, 0);
+  } catch (...) {
+    delete plan;
+    return set_error(PSA_ERR_ALLOC, "out of memory for the plan image");
+  }
+  auto put32 = [&](int64_t at, int64_t idx, int64_t v) {
+    int32_t x = (int32_t)v;
+    std::memcpy(img.data() + at + idx * 4, &x, 4);
+  };
+  if (!items.empty()) std::memcpy(img.data() + L.items, items.data(), items.size() * sizeof(WorkItem));
+  for (int g = 0; g <= G && G > 0; ++g) put32(L.group_page_off, g, b->group_page_off[g]);
+  if (G == 0) put32(L.group_page_off, 0, 0);
+  for (int64_t t = 0; t < n_gpages; ++t) put32(L.group_pages, t, b->group_pages[t]);
+  for (int g = 0; g < G; ++g) put32(L.group_len, g, b->group_prefix_len[g]);
+  for (int g = 0; g <= G; ++g) put32(L.member_off, g, member_off[g]);
+  for (size_t t = 0; t < members.size(); ++t) put32(L.members, t, members[t]);
+  for (int i = 0; i <= N && N > 0; ++i) put32(L.query_page_off, i, b->query_page_off[i]);
+  if (N == 0) put32(L.query_page_off, 0, 0);
+  for (int64_t t = 0; t < n_qpages; ++t) put32(L.query_pages, t, b->query_pages[t]);
+  for (int i = 0; i < N; ++i) {
+    put32(L.query_group, i, b->query_group[i]);
+    put32(L.query_dlen, i, b->query_distinct_len[i]);
+    put32(L.expected, i, expected[i]);
+    put32(L.slot_off, i, slot_off[i]);
+  }
+  // counters stay zero
+
+  // ---- statistics ----
+  psa_plan_info& info = plan->info;
+  info.workspace_bytes = (size_t)L.total_bytes;
+  info.num_items = (int64_t)items.size();
+  info.num_prefix_items = n_prefix_items;
+  info.num_matvec_items = n_matvec_items;
+  info.num_partial_slots = slots * hkv;
+  int64_t logical = 0, processed = 0, prefix_logical = 0;
+  for (int g = 0; g < G; ++g)
+    if (member_off[g + 1] > member_off[g]) processed += b->group_prefix_len[g];
+  for (int i = 0; i < N; ++i) {
+    const int g = b->query_group[i];
+    const int64_t lp = g >= 0 ? b->group_prefix_len[g] : 0;
+    logical += lp + b->query_distinct_len[i];
+    prefix_logical += lp;
+    processed += b->query_distinct_len[i];
+  }
+  info.logical_tokens = logical;
+  info.processed_tokens = processed;
+  info.saved_tokens = logical - processed;
+  int64_t prefix_once = 0, distinct_tok = 0;
+  for (int g = 0; g < G; ++g)
+    if (member_off[g + 1] > member_off[g]) prefix_once += b->group_prefix_len[g];
+  for (int i = 0; i < N; ++i) distinct_tok += b->query_distinct_len[i];
+  const double tok_bytes = (double)hkv * d * 2 * e;
+  info.prefix_kv_bytes = (double)prefix_once * tok_bytes;
+  info.distinct_kv_bytes = (double)distinct_tok * tok_bytes;
+  info.algorithmic_bytes = info.prefix_kv_bytes + info.distinct_kv_bytes + (double)N * c.num_q_heads * d * e +
+                           (double)N * c.num_q_heads * d * (c.out_dtype == PSA_BF16 ? 2 : 4);
+  info.algorithmic_flops = 4.0 * d * c.num_q_heads * (double)logical;
+  info.prefix_flops = 4.0 * d * c.num_q_heads * (double)prefix_logical;
+
+  plan->items = std::move(items);
+  plan->expected = std::move(expected);
+  plan->slot_off = std::move(slot_off);
+  *out = plan;
+  return PSA_OK;
+}
+
+}  // namespace psa

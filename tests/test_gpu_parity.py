@@ -1,0 +1,255 @@
+"""GPU parity: the fused HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases are compared element by element on every output; the full-size
+workloads run in the bench's launch configuration and are compared on sampled
+queries the oracle computes one by one.  Tolerances: bf16 inputs max |err|
+<= 1e-2 and relative L2 <= 5e-3; fp32 inputs 1e-5 for both.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import prefix_shared_decode_amd as P
+from workloads import build_single_level, build_two_level, fill_stale, make_workload
+
+from gpu_helpers import (assert_close, assert_lse_close, log, oracle_all, run, sampled_oracle, to_host64,
+                         values)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_full(wl, batch, q, k, v, what, out_dtype="f32", lse=True, **kw):
+    log(f"case {what}: queries={len(batch['query_group'])} plan={kw}")
+    step, out, m, l = run(wl, batch, q, k, v, out_dtype=out_dtype, **kw)
+    O, M, L = oracle_all(wl, batch, q, k, v)
+    assert_close(to_host64(out), O, wl.dtype if out_dtype == "f32" else "bf16", what)
+    if lse:
+        assert_lse_close(m, l, M, L, 1e-5 if wl.dtype == "f32" else 2e-4)
+    return step, out, m, l
+
+
+# ---------------- the tiny fp32 workload, exactly ----------------
+
+def test_tiny_fp32_exact_config():
+    wl = make_workload("tiny_fp32_1x4")
+    q, k, v = values(wl)
+    _check_full(wl, wl.batch, q, k, v, "tiny_fp32_1x4")
+
+
+# ---------------- reduced shapes of the bf16 workloads ----------------
+
+SMALL = {
+    # Llama-3-8B heads (32/8, d128): 2 groups x 20 requests, ragged prefix, multi-chunk
+    "gqa4_groups": dict(hq=32, hkv=8, d=128, groups=[(300, 20, (0, 200)), (77, 9, (1, 90))], ung=(3, (1, 300))),
+    # LongChat-like MHA (40/40 heads): one group, prefix spans several chunks
+    "mha_group": dict(hq=40, hkv=40, d=128, groups=[(700, 24, (5, 100))], ung=(0, (1, 2))),
+    # no sharing: pure paged decode with several distinct chunks
+    "no_sharing": dict(hq=32, hkv=8, d=128, groups=[], ung=(12, (1, 1500))),
+    # head_dim 64 and GQA ratio 8
+    "d64_r8": dict(hq=16, hkv=2, d=64, groups=[(130, 6, (0, 70))], ung=(2, (1, 40))),
+    # GQA ratio 2 with a group just above the MFMA threshold
+    "r2_tail_rows": dict(hq=8, hkv=4, d=128, groups=[(33, 9, (0, 20))], ung=(1, (1, 17))),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("opts", [dict(), dict(prefix_chunk_tokens=128, distinct_chunk_tokens=64, mfma_tile_rows=32),
+                                  dict(flags=P.FORCE_MATVEC)], ids=["default", "small_chunks", "matvec_only"])
+def test_small_bf16(name, opts):
+    s = SMALL[name]
+    wl = build_single_level(name, s["hq"], s["hkv"], s["d"], "bf16", s["groups"], s["ung"], seed=11, spare_pages=5)
+    q, k, v = values(wl)
+    _check_full(wl, wl.batch, q, k, v, f"{name}/{opts}", **opts)
+
+
+def test_two_level_small_flattened():
+    wl = build_two_level("two_level_small", 32, 8, 128, "bf16", 2, 64, 3, 128, 4, (0, 60), seed=5)
+    batch, saved = P.psa_flatten_prefix_tree(wl.tree)
+    assert saved == 6 * 192 * 3
+    q, k, v = values(wl)
+    log("case two_level_small")
+    _, out, m, l = run(wl, batch, q, k, v)
+    # the oracle reads each query's context straight from the tree
+    O, M, L = oracle.decode_attention(to_host64(q), to_host64(k), to_host64(v),
+                                      oracle.flatten_tree(wl.tree, [-1] * len(wl.tree["query_node"])))
+    assert_close(to_host64(out), O, "bf16", "two_level_small")
+
+
+# ---------------- edge cases ----------------
+
+def test_stale_padding_is_masked():
+    wl = build_single_level("stale", 32, 8, 128, "bf16", [(37, 17, (0, 35))], (3, (1, 20)), seed=3)
+    q, k, v = values(wl)
+    fill_stale(wl, k, v, 1.0e4)
+    _check_full(wl, wl.batch, q, k, v, "stale+-1e4")
+    _check_full(wl, wl.batch, q, k, v, "stale+-1e4 matvec", flags=P.FORCE_MATVEC)
+
+
+def test_single_token_and_empty_distinct():
+    # prefix of one token with empty distinct parts; distinct of one token without prefix
+    wl = build_single_level("tiny_ctx", 8, 2, 128, "bf16", [(1, [0, 0, 0, 0, 1, 0, 0, 0]), (16, [0] * 5)],
+                            [1, 1, 16, 17], seed=4)
+    q, k, v = values(wl)
+    _check_full(wl, wl.batch, q, k, v, "single-token", mfma_min_rows=4)
+
+
+def test_fp32_larger_and_scale():
+    wl = build_single_level("f32_mix", 8, 4, 128, "f32", [(200, 10, (0, 90))], (4, (1, 600)), seed=8)
+    q, k, v = values(wl)
+    _check_full(wl, wl.batch, q, k, v, "f32 d128")
+    log("case f32 custom scale")
+    _, out, m, l = run(wl, wl.batch, q, k, v, sm_scale=0.3)
+    O, M, L = oracle_all(wl, wl.batch, q, k, v, sm_scale=0.3)
+    assert_close(to_host64(out), O, "f32", "f32 scale 0.3")
+
+
+def test_bf16_output():
+    wl = build_single_level("bf16_out", 32, 8, 128, "bf16", [(256, 12, (4, 64))], (2, (1, 99)), seed=9)
+    q, k, v = values(wl)
+    log("case bf16 output")
+    _, out, _, _ = run(wl, wl.batch, q, k, v, out_dtype="bf16")
+    O, _, _ = oracle_all(wl, wl.batch, q, k, v)
+    assert_close(to_host64(out), O, "bf16", "bf16 out")
+
+
+def test_empty_batch_is_a_no_op():
+    import torch
+
+    wl = build_single_level("empty", 32, 8, 128, "bf16", [], [], seed=0)
+    step = P.DecodeStep(P.make_config(32, 8, 128, 1, "bf16"), wl.batch)
+    z = torch.zeros((0, 32, 128), dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros((1, 8, 16, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((0, 32, 128), dtype=torch.float32, device="cuda")
+    step(z, pool, pool, out)
+    torch.cuda.synchronize()
+
+
+# ---------------- partials, merge, determinism ----------------
+
+def test_prefix_and_distinct_partials_merge_to_fused():
+    import torch
+
+    wl = build_single_level("split", 32, 8, 128, "bf16", [(160, 12, (0, 80)), (48, 3, (3, 9))], (3, (1, 50)), seed=2)
+    q, k, v = values(wl)
+    log("case PREFIX_ONLY / DISTINCT_ONLY / psa_merge")
+    _, op, mp, lp = run(wl, wl.batch, q, k, v, flags=P.PREFIX_ONLY)
+    _, od, md, ld = run(wl, wl.batch, q, k, v, flags=P.DISTINCT_ONLY)
+    _, of, mf, lf = run(wl, wl.batch, q, k, v)
+    # each partial against the oracle's partial over the same token range
+    b = wl.batch
+    prefix_only = dict(b, query_distinct_len=np.zeros_like(b["query_distinct_len"]))
+    distinct_only = dict(b, query_group=np.full_like(b["query_group"], -1))
+    qh, kh, vh = to_host64(q), to_host64(k), to_host64(v)
+    has_p = b["query_group"] >= 0
+    has_d = b["query_distinct_len"] > 0
+    Op, Mp, Lp = oracle.decode_attention(qh[has_p], kh, vh, {**prefix_only, **_rows(prefix_only, has_p)})
+    assert_close(to_host64(op)[has_p], Op, "bf16", "prefix partial")
+    assert np.all(to_host64(lp)[~has_p] == 0) and np.all(to_host64(mp)[~has_p] == -np.inf)
+    assert np.all(to_host64(op)[~has_p] == 0)
+    Od, Md, Ld = oracle.decode_attention(qh[has_d], kh, vh, {**distinct_only, **_rows(distinct_only, has_d)})
+    assert_close(to_host64(od)[has_d], Od, "bf16", "distinct partial")
+    # psa_merge of the two partials equals the fused result
+    n, hq, d = op.shape
+    o = torch.empty_like(op)
+    m = torch.empty_like(mp)
+    l = torch.empty_like(lp)
+    P.psa_merge(op.view(-1, d), mp.view(-1), lp.view(-1), od.view(-1, d), md.view(-1), ld.view(-1),
+                o.view(-1, d), m.view(-1), l.view(-1))
+    torch.cuda.synchronize()
+    mx = float((o - of).abs().max())
+    log(f"  merge vs fused max diff {mx:.3e}")
+    assert mx <= 2e-6
+    # in-place merge (outputs alias the a inputs)
+    P.psa_merge(op.view(-1, d), mp.view(-1), lp.view(-1), od.view(-1, d), md.view(-1), ld.view(-1),
+                op.view(-1, d), mp.view(-1), lp.view(-1))
+    torch.cuda.synchronize()
+    assert torch.equal(op, o) and torch.equal(mp, m) and torch.equal(lp, l)
+
+
+def _rows(batch, mask):
+    """Restrict a batch's query arrays to the queries in ``mask``."""
+    idx = np.nonzero(mask)[0]
+    qoff = batch["query_page_off"]
+    pages, off = [], [0]
+    for i in idx:
+        pages.extend(batch["query_pages"][qoff[i]:qoff[i + 1]])
+        off.append(len(pages))
+    return {"query_group": batch["query_group"][idx], "query_distinct_len": batch["query_distinct_len"][idx],
+            "query_page_off": np.asarray(off, np.int64), "query_pages": np.asarray(pages, np.int32)}
+
+
+def test_psa_merge_against_oracle():
+    import torch
+
+    rng = np.random.default_rng(0)
+    rows, d = 300, 128
+    Oa, Ob = rng.standard_normal((rows, d)), rng.standard_normal((rows, d))
+    ma, mb = rng.standard_normal(rows) * 3, rng.standard_normal(rows) * 3
+    la, lb = rng.uniform(0.5, 40, rows), rng.uniform(0.5, 40, rows)
+    # empty partials on some rows (identity), both empty on one
+    ma[:5], la[:5], Oa[:5] = -np.inf, 0, 0
+    mb[3:8], lb[3:8], Ob[3:8] = -np.inf, 0, 0
+    Oe, Me, Le = oracle.merge_partials((Oa, ma, la), (Ob, mb, lb))
+    t = lambda x: torch.tensor(x, dtype=torch.float32, device="cuda")  # noqa: E731
+    o, m, l = t(np.zeros((rows, d))), t(np.zeros(rows)), t(np.zeros(rows))
+    log("case psa_merge vs oracle")
+    P.psa_merge(t(Oa), t(ma), t(la), t(Ob), t(mb), t(lb), o, m, l)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_host64(o), Oe, atol=2e-6, rtol=0)
+    np.testing.assert_allclose(to_host64(l), Le, rtol=2e-6)
+    assert np.all(to_host64(m)[3:5] == -np.inf)
+
+
+def test_deterministic_and_reusable_workspace():
+    import torch
+
+    wl = build_single_level("det", 32, 8, 128, "bf16", [(400, 30, (0, 300))], (4, (1, 900)), seed=6)
+    q, k, v = values(wl)
+    log("case determinism x20, shuffled order, poisoned slots")
+    step, out, m, l = run(wl, wl.batch, q, k, v, prefix_chunk_tokens=128, distinct_chunk_tokens=128)
+    ref = out.clone()
+    for _ in range(20):  # the same workspace: counters reset themselves
+        step(q, k, v, out, m, l)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    _, out2, _, _ = run(wl, wl.batch, q, k, v, prefix_chunk_tokens=128, distinct_chunk_tokens=128,
+                        flags=P.NO_XCD_ORDER)
+    assert torch.equal(out2, ref)
+    _, out3, _, _ = run(wl, wl.batch, q, k, v, prefix_chunk_tokens=128, distinct_chunk_tokens=128,
+                        flags=P.DEBUG_POISON)
+    assert torch.equal(out3, ref)
+
+
+# ---------------- full-size workloads, sampled ----------------
+
+FULL = ["llama3_8b_8x100", "longchat13b_1x256", "no_sharing_512", "two_level_4x16x16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    import torch
+
+    wl = make_workload(name)
+    batch = wl.batch
+    if wl.tree is not None:
+        batch, _ = P.psa_flatten_prefix_tree(wl.tree)
+    log(f"case full {name}: generating values")
+    q, k, v = values(wl)
+    log(f"case full {name}: launching")
+    _, out, m, l = run(wl, batch, q, k, v)
+    n = len(batch["query_group"])
+    rng = np.random.default_rng(1)
+    sample = sorted(rng.choice(n, size=min(12, n), replace=False).tolist() + [0, n - 1])
+    sample = sorted(set(sample))
+    heads = None if wl.num_kv_heads <= 8 else sorted(rng.choice(wl.num_q_heads, size=6, replace=False).tolist())
+    log(f"case full {name}: oracle on {len(sample)} queries")
+    O, M, L = sampled_oracle(wl, batch, q, k, v, sample, heads)
+    got = to_host64(out)[sample]
+    gm, gl = to_host64(m)[sample], to_host64(l)[sample]
+    if heads is not None:
+        got = got[:, heads].reshape(-1, wl.head_dim)
+        gm, gl = gm[:, heads].reshape(-1), gl[:, heads].reshape(-1)
+    assert_close(got, O, "bf16", f"full {name} sampled")
+    assert np.abs((gm + np.log(gl)) - (M + np.log(L))).max() <= 2e-4
+    assert torch.isfinite(out).all()

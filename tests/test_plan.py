@@ -1,0 +1,324 @@
+"""Host-side tests of the C ABI (CPU only; no kernel is launched).
+
+* the library loads and exports every function include/*.h declares;
+* the plan covers every (query, q head, context token) exactly once and its
+  partial-slot bookkeeping is consistent;
+* every validation error is reachable and reported with its status;
+* plan statistics equal the workload bookkeeping;
+* the C++ prefix-tree flattening reaches the oracle's (brute-force pinned)
+  optimum and keeps every query's token sequence.
+"""
+
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import prefix_shared_decode_amd as P
+from workloads import algorithmic_cost, build_single_level, build_two_level, make_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in ("psa.h", "psa_debug.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(psa_[a-z_]+)\s*\(", text):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert {"psa_build_plan", "psa_decode_attention", "psa_merge"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    assert declared <= exported, declared - exported
+    L = P.lib()
+    for name in declared:
+        assert hasattr(L, name)
+    assert set(P.EXPORTS) == declared
+    assert L.psa_version() == 1
+
+
+def _cfg(wl, **kw):
+    return P.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.dtype, **kw)
+
+
+def _coverage(wl, plan):
+    """Expand the work list to (query, kv head) -> list of (segment, tok_begin, tok_end, slot)."""
+    b = wl.batch
+    r = wl.num_q_heads // wl.num_kv_heads
+    cov = {}
+    members = {}
+    for i, g in enumerate(b["query_group"]):
+        if g >= 0:
+            members.setdefault(int(g), []).append(i)
+    for kind, kvh, ident, tb, te, rb, rc, slot in plan.items():
+        if kind in (0, 1):
+            cov.setdefault((ident, kvh), []).append(("d" if kind == 0 else "p", tb, te, slot))
+        elif kind == 2:
+            assert rb % r == 0 and rc % r == 0 and 0 < rc <= 128
+            for mi in range(rb // r, (rb + rc) // r):
+                cov.setdefault((members[ident][mi], kvh), []).append(("p", tb, te, slot))
+        elif kind == 3:
+            for kvh2 in range(wl.num_kv_heads):
+                cov.setdefault((ident, kvh2), []).append(("e", 0, 0, 0))
+    return cov
+
+
+def _check_coverage(wl, plan, prefix=True, distinct=True):
+    b = wl.batch
+    cov = _coverage(wl, plan)
+    expected, slot_off = plan.queries()
+    for i in range(wl.num_queries):
+        g = int(b["query_group"][i])
+        lp = int(b["group_prefix_len"][g]) if g >= 0 else 0
+        ld = int(b["query_distinct_len"][i])
+        for kvh in range(wl.num_kv_heads):
+            parts = cov.get((i, kvh), [])
+            want_p = set(range(lp)) if prefix else set()
+            want_d = set(range(ld)) if distinct else set()
+            got_p, got_d = [], []
+            for seg, tb, te, _ in parts:
+                assert tb % 16 == 0
+                (got_p if seg == "p" else got_d if seg == "d" else []).extend(range(tb, te))
+            assert sorted(got_p) == sorted(want_p)
+            assert sorted(got_d) == sorted(want_d)
+            real = [x for x in parts if x[0] != "e"]
+            assert expected[i] == len(real)
+            if not real:
+                assert any(x[0] == "e" for x in parts)
+            assert sorted(x[3] for x in real) == list(range(len(real)))
+            # prefix partials come first
+            assert all(x[3] < sum(1 for y in real if y[0] == "p") for x in real if x[0] == "p")
+            assert (slot_off[i] >= 0) == (expected[i] >= 2)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_plan_covers_every_token_once(seed, dtype):
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 4]))
+    r = int(rng.choice([1, 2, 4, 8]))
+    groups = [(int(rng.integers(0, 200)), int(rng.integers(1, 40)), (0, int(rng.integers(1, 300)))) for _ in range(3)]
+    wl = build_single_level("t", hkv * r, hkv, 64, dtype, groups, (4, (1, 700)), seed=seed)
+    # make sure no query has an empty context
+    for i in range(wl.num_queries):
+        g = wl.batch["query_group"][i]
+        if (wl.batch["group_prefix_len"][g] if g >= 0 else 0) + wl.batch["query_distinct_len"][i] == 0:
+            pytest.skip("drew an empty context")
+    for kw in ({}, {"prefix_chunk_tokens": 48, "distinct_chunk_tokens": 32, "mfma_tile_rows": 32},
+               {"flags": P.FORCE_MATVEC}, {"flags": P.NO_XCD_ORDER, "mfma_min_rows": 1}):
+        plan = P.psa_build_plan(_cfg(wl), wl.batch, **kw)
+        _check_coverage(wl, plan)
+    plan = P.psa_build_plan(_cfg(wl), wl.batch, flags=P.PREFIX_ONLY)
+    _check_coverage(wl, plan, distinct=False)
+    plan = P.psa_build_plan(_cfg(wl), wl.batch, flags=P.DISTINCT_ONLY)
+    _check_coverage(wl, plan, prefix=False)
+
+
+def test_mfma_tiles_only_for_bf16_groups_with_enough_rows():
+    wl = build_single_level("t", 4, 2, 128, "bf16", [(64, 3, (1, 5)), (64, 5, (1, 5))], [], seed=1)
+    plan = P.psa_build_plan(_cfg(wl), wl.batch)  # rows 6 and 10 < 16
+    assert plan.info()["num_prefix_items"] == 0
+    plan = P.psa_build_plan(_cfg(wl), wl.batch, mfma_min_rows=8)
+    it = plan.items()
+    assert set(it[it[:, 0] == 2][:, 2]) == {1}
+    wl32 = build_single_level("t", 4, 2, 128, "f32", [(64, 30, (1, 5))], [], seed=1)
+    assert P.psa_build_plan(_cfg(wl32), wl32.batch).info()["num_prefix_items"] == 0
+
+
+def test_xcd_order_keeps_prefix_sets_on_one_xcd():
+    wl = make_workload("llama3_8b_8x100")
+    plan = P.psa_build_plan(_cfg(wl), wl.batch)
+    it = plan.items()
+    pos = {}
+    for idx, row in enumerate(it):
+        if row[0] == 2:
+            pos.setdefault((row[2], row[1], row[3]), []).append(idx)
+    assert len(pos) == 64 and all(len(v) == 4 for v in pos.values())
+    for v in pos.values():
+        assert len({x % 8 for x in v}) == 1
+    # longest-first within the list: all MFMA tiles come before mat-vec tiles
+    kinds = it[:, 0]
+    assert kinds[: 256].tolist() == [2] * 256
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_1x4", "llama3_8b_8x100", "longchat13b_1x256", "no_sharing_512"])
+def test_plan_statistics_match_bookkeeping(name):
+    wl = make_workload(name)
+    plan = P.psa_build_plan(_cfg(wl), wl.batch)
+    info = plan.info()
+    cost = algorithmic_cost(wl)
+    assert info["algorithmic_bytes"] == cost["bytes"]
+    assert info["algorithmic_flops"] == cost["flops"]
+    assert info["prefix_flops"] == cost["flops_prefix"]
+    assert info["logical_tokens"] == cost["logical_tokens"]
+    assert info["processed_tokens"] == cost["processed_tokens"]
+    assert info["saved_tokens"] == cost["logical_tokens"] - cost["processed_tokens"]
+
+
+def _tiny():
+    return build_single_level("t", 4, 2, 64, "bf16", [(40, 2, (1, 9))], [5], seed=0)
+
+
+def _status(fn):
+    with pytest.raises(P.PsaError) as e:
+        fn()
+    return e.value.status_name
+
+
+def test_error_paths():
+    wl = _tiny()
+    b = wl.batch
+    c = _cfg(wl)
+    mk = lambda cfg=c, batch=b, **kw: P.psa_build_plan(cfg, batch, **kw)  # noqa: E731
+    cfg = lambda **kw: P.make_config(**{**dict(num_q_heads=4, num_kv_heads=2, head_dim=64,  # noqa: E731
+                                               num_pages=wl.num_pages, kv_dtype="bf16"), **kw})
+    assert _status(lambda: mk(cfg(num_q_heads=5))) == "PSA_ERR_INVALID_ARGUMENT"
+    assert _status(lambda: mk(cfg(num_q_heads=32, num_kv_heads=2))) == "PSA_ERR_UNSUPPORTED"  # r = 16
+    assert _status(lambda: mk(cfg(head_dim=96))) == "PSA_ERR_UNSUPPORTED"
+    assert _status(lambda: mk(cfg(page_size=32))) == "PSA_ERR_UNSUPPORTED"
+    assert _status(lambda: mk(cfg(num_pages=0))) == "PSA_ERR_INVALID_ARGUMENT"
+    bad = dict(b, query_pages=np.where(np.arange(len(b["query_pages"])) == 0, wl.num_pages, b["query_pages"]))
+    assert _status(lambda: mk(batch=bad)) == "PSA_ERR_OUT_OF_RANGE"
+    bad = dict(b, query_distinct_len=b["query_distinct_len"] + 16)
+    assert _status(lambda: mk(batch=bad)) == "PSA_ERR_OUT_OF_RANGE"
+    bad = dict(b, query_distinct_len=-b["query_distinct_len"])
+    assert _status(lambda: mk(batch=bad)) == "PSA_ERR_INVALID_ARGUMENT"
+    bad = dict(b, query_page_off=b["query_page_off"][::-1].copy())
+    assert _status(lambda: mk(batch=bad)) == "PSA_ERR_INVALID_ARGUMENT"
+    bad = dict(b, query_group=np.full_like(b["query_group"], 7))
+    assert _status(lambda: mk(batch=bad)) == "PSA_ERR_INVALID_ARGUMENT"
+    # empty context: an ungrouped query with no distinct tokens
+    bad = dict(b, query_distinct_len=np.where(b["query_group"] < 0, 0, b["query_distinct_len"]).astype(np.int32))
+    assert _status(lambda: mk(batch=bad)) == "PSA_ERR_INVALID_ARGUMENT"
+    P.psa_build_plan(c, bad, flags=P.PREFIX_ONLY)  # allowed when only the prefix is covered
+    assert _status(lambda: mk(flags=P.PREFIX_ONLY | P.DISTINCT_ONLY)) == "PSA_ERR_INVALID_ARGUMENT"
+    assert _status(lambda: mk(prefix_chunk_tokens=20)) == "PSA_ERR_INVALID_ARGUMENT"
+    assert _status(lambda: mk(mfma_tile_rows=256)) == "PSA_ERR_INVALID_ARGUMENT"
+    assert _status(lambda: mk(flags=0x400)) == "PSA_ERR_INVALID_ARGUMENT"
+    # messages name the problem
+    with pytest.raises(P.PsaError, match="page id"):
+        mk(batch=dict(b, group_pages=np.full_like(b["group_pages"], -3)))
+
+
+def test_decode_rejects_host_pointers_and_small_workspace_without_launching():
+    """Calls that must fail before any kernel: they touch only host-side checks."""
+    import ctypes as C
+
+    L = P.lib()
+    wl = _tiny()
+    plan = P.psa_build_plan(_cfg(wl), wl.batch)
+    ws_bytes = plan.info()["workspace_bytes"]
+    host = (C.c_uint8 * 4096)()
+    st = L.psa_decode_attention(plan.handle, C.addressof(host), C.addressof(host), C.addressof(host),
+                                C.addressof(host), None, None, C.addressof(host), ws_bytes - 1, None)
+    assert P._lib.STATUS[st] == "PSA_ERR_WORKSPACE_TOO_SMALL"
+    st = L.psa_plan_upload(plan.handle, C.addressof(host), ws_bytes - 1, None)
+    assert P._lib.STATUS[st] == "PSA_ERR_WORKSPACE_TOO_SMALL"
+    st = L.psa_decode_attention(plan.handle, C.addressof(host), C.addressof(host), C.addressof(host),
+                                C.addressof(host), None, None, C.addressof(host), ws_bytes, None)
+    assert P._lib.STATUS[st] == "PSA_ERR_INVALID_ARGUMENT"  # workspace never uploaded
+    st = L.psa_merge(4, 96, *([None] * 9), None)
+    assert P._lib.STATUS[st] == "PSA_ERR_UNSUPPORTED"
+    st = L.psa_merge(4, 64, *([None] * 9), None)
+    assert P._lib.STATUS[st] == "PSA_ERR_INVALID_ARGUMENT"
+    assert L.psa_merge(0, 64, *([None] * 9), None) == 0
+
+
+def test_empty_batch_plans_no_work():
+    wl = build_single_level("t", 2, 1, 64, "bf16", [], [], seed=0)
+    plan = P.psa_build_plan(_cfg(wl), wl.batch)
+    assert plan.info()["num_items"] == 0
+
+
+# ---------------- flattening ----------------
+
+def _random_tree(seed, page=16):
+    rng = np.random.default_rng(seed)
+    m = int(rng.integers(1, 7))
+    parent = [-1] + [int(rng.integers(-1, d)) for d in range(1, m)]
+    lens = [page * int(x) for x in rng.integers(1, 6, size=m)]
+    n = int(rng.integers(1, 9))
+    qn = [int(x) for x in rng.integers(-1, m, size=n)]
+    dl = [int(x) for x in rng.integers(0, 40, size=n)]
+    perm = rng.permutation(10_000)
+    pos = 0
+    node_pages, noff = [], [0]
+    for ln in lens:
+        node_pages += [int(x) for x in perm[pos:pos + ln // page]]
+        pos += ln // page
+        noff.append(len(node_pages))
+    qpages, qoff = [], [0]
+    for x in dl:
+        k = -(-x // page)
+        qpages += [int(y) for y in perm[pos:pos + k]]
+        pos += k
+        qoff.append(len(qpages))
+    return {"page_size": page, "node_parent": parent, "node_len": lens, "node_page_off": noff,
+            "node_pages": node_pages, "query_node": qn, "query_distinct_len": dl, "query_page_off": qoff,
+            "query_pages": qpages}
+
+
+def _tree_context(t, i):
+    nodes = []
+    x = int(t["query_node"][i])
+    while x >= 0:
+        nodes.append(x)
+        x = int(t["node_parent"][x])
+    pages = [p for d in reversed(nodes) for p in t["node_pages"][t["node_page_off"][d]:t["node_page_off"][d + 1]]]
+    pages += list(t["query_pages"][t["query_page_off"][i]:t["query_page_off"][i + 1]])
+    return pages, sum(int(t["node_len"][d]) for d in nodes) + int(t["query_distinct_len"][i])
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_flatten_matches_oracle_optimum(seed):
+    t = _random_tree(seed)
+    batch, saved = P.psa_flatten_prefix_tree(t)
+    best, _ = oracle.maximize_reuse(t["node_parent"], t["node_len"], t["query_node"])
+    assert saved == best
+    # the returned groups realise that saving and keep every query's tokens
+    qg = batch["query_group"]
+    got = sum(int(batch["group_prefix_len"][g]) * (int((qg == g).sum()) - 1) for g in range(len(batch["group_prefix_len"])))
+    assert got == best
+    assert all((qg == g).sum() >= 2 for g in range(len(batch["group_prefix_len"])))
+    for i in range(len(t["query_node"])):
+        pages, n = _tree_context(t, i)
+        segs = oracle.query_context(batch, i)
+        flat = []
+        total = 0
+        for p, ln in segs:
+            assert ln % 16 == 0 or (p is segs[-1][0])
+            flat += list(p[: -(-ln // 16)])
+            total += ln
+        assert total == n
+        assert flat == pages[: -(-n // 16)]
+
+
+def test_flatten_two_level_workload_closed_form():
+    wl = build_two_level("t", 32, 8, 128, "bf16", 4, 1024, 16, 2048, 16, (32, 256))
+    batch, saved = P.psa_flatten_prefix_tree(wl.tree)
+    assert saved == 64 * 3072 * 15
+    assert len(batch["group_prefix_len"]) == 64 and set(batch["group_prefix_len"]) == {3072}
+    cfg = P.make_config(32, 8, 128, wl.num_pages, "bf16")
+    info = P.psa_build_plan(cfg, batch).info()
+    assert info["saved_tokens"] == saved
+
+
+def test_flatten_error_paths():
+    t = _random_tree(3)
+    assert _status(lambda: P.psa_flatten_prefix_tree(dict(t, node_len=[x + 1 for x in t["node_len"]]))) == \
+        "PSA_ERR_INVALID_ARGUMENT"
+    bad = dict(t, node_parent=[len(t["node_parent"])] + list(t["node_parent"][1:]))
+    assert _status(lambda: P.psa_flatten_prefix_tree(bad)) == "PSA_ERR_INVALID_ARGUMENT"
+    if len(t["node_parent"]) >= 2:
+        cyc = dict(t, node_parent=[1, 0] + list(t["node_parent"][2:]))
+        assert _status(lambda: P.psa_flatten_prefix_tree(cyc)) == "PSA_ERR_INVALID_ARGUMENT"
+    assert _status(lambda: P.psa_flatten_prefix_tree(t, page_size=8)) == "PSA_ERR_UNSUPPORTED"
