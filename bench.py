@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--distinct-chunk", type=int, default=0)
     ap.add_argument("--tile-rows", type=int, default=0)
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -181,6 +183,13 @@ def main():
         P.psa_decode_attention(plan, q, k, v, out, ws)
 
     flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    if args.copy_calib_mib > 0:
+        # a plain copy kernel of known size: reads and writes exactly this many bytes
+        src = torch.ones(args.copy_calib_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

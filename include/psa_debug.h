@@ -12,12 +12,14 @@ extern "C" {
 #endif
 
 /* Copy the plan's work list (the order the fused launch runs it in) to host
- * memory `out`: 8 int32 per item = {kind, kv_head, id, tok_begin, tok_end,
- * row_begin, row_count, slot}; kind 0 = mat-vec over a query's distinct pages,
- * 1 = mat-vec over its group's prefix pages, 2 = MFMA prefix tile over rows
- * [row_begin, row_begin + row_count) of group `id` (row = member * Hq/Hkv +
- * head in kv group), 3 = empty partial of query `id`.  capacity_items must be
- * >= psa_plan_info.num_items. */
+ * memory `out`: psa_plan_info.num_items units (one per workgroup) of 4 items,
+ * 8 int32 per item = {kind | chunk << 8, kv_head, id, tok_begin, tok_end,
+ * page_base, a, b}.  kind 0 = nothing, 1 = mat-vec over query `id`'s pages
+ * (page_base indexes group pages followed by query pages; a = partials of the
+ * query, b = its partial slot or -1), 2 = MFMA prefix tile over rows
+ * [a, a + b) of group `id` (row = member * Hq/Hkv + head in kv group; only
+ * as the first item of a unit), 3 = empty partial of query `id`.
+ * capacity_items must be >= 4 * num_items. */
 psa_status psa_plan_debug_items(const psa_plan* plan, int32_t* out, int64_t capacity_items);
 
 /* Per query: number of partial results merged into its output (1 = the one

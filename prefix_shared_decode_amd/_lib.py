@@ -171,8 +171,8 @@ class Plan:
         return psa_plan_get_info(self)
 
     def items(self):
-        """Work list as an [num_items, 8] int32 array (psa_debug.h)."""
-        n = self.info()["num_items"]
+        """Work list as an [num_units * 4, 8] int32 array (psa_debug.h)."""
+        n = 4 * self.info()["num_items"]
         out = np.zeros((max(n, 1), 8), dtype=np.int32)
         _check(lib().psa_plan_debug_items(self.handle, out.ctypes.data_as(_I32P), n))
         return out[:n]

@@ -158,22 +158,17 @@ psa_status psa_decode_attention(const psa_plan* plan, const void* d_q, const voi
   p.out_m = d_out_m;
   p.out_l = d_out_l;
   p.items = reinterpret_cast<const psa::WorkItem*>(ws + L.items);
-  p.group_page_off = reinterpret_cast<const int32_t*>(ws + L.group_page_off);
-  p.group_pages = reinterpret_cast<const int32_t*>(ws + L.group_pages);
-  p.group_len = reinterpret_cast<const int32_t*>(ws + L.group_len);
+  p.pages = reinterpret_cast<const int32_t*>(ws + L.pages);
   p.member_off = reinterpret_cast<const int32_t*>(ws + L.member_off);
   p.members = reinterpret_cast<const int32_t*>(ws + L.members);
-  p.query_page_off = reinterpret_cast<const int32_t*>(ws + L.query_page_off);
-  p.query_pages = reinterpret_cast<const int32_t*>(ws + L.query_pages);
-  p.query_group = reinterpret_cast<const int32_t*>(ws + L.query_group);
-  p.query_dlen = reinterpret_cast<const int32_t*>(ws + L.query_dlen);
   p.expected = reinterpret_cast<const int32_t*>(ws + L.expected);
   p.slot_off = reinterpret_cast<const int32_t*>(ws + L.slot_off);
   p.counters = reinterpret_cast<int32_t*>(ws + L.counters);
   p.part_o = reinterpret_cast<float*>(ws + L.part_o);
   p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
-  p.num_items = (int32_t)plan->items.size();
-  p.num_queries = (int32_t)plan->expected.size();
+  p.part_o_bytes = plan->part_o_bytes;
+  p.part_ml_bytes = plan->part_ml_bytes;
+  p.num_units = (int32_t)plan->num_units;
   p.hq = plan->cfg.num_q_heads;
   p.hkv = plan->cfg.num_kv_heads;
   p.scale_log2 = plan->sm_scale * 1.4426950408889634f;

@@ -80,6 +80,8 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   if (o.prefix_chunk_tokens < 0 || o.prefix_chunk_tokens % c.page_size || o.distinct_chunk_tokens < 0 ||
       o.distinct_chunk_tokens % c.page_size)
     return set_error(PSA_ERR_INVALID_ARGUMENT, "chunk sizes must be positive multiples of page_size");
+  if (o.prefix_chunk_tokens > kMaxPrefixChunk || o.distinct_chunk_tokens > kMaxMatvecPages * 16)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "chunk sizes are limited to 2048 (prefix) and 1024 (distinct) tokens");
   if (o.mfma_min_rows < 0) return set_error(PSA_ERR_INVALID_ARGUMENT, "mfma_min_rows must be >= 0");
   if (o.mfma_tile_rows < 16 || o.mfma_tile_rows > 128 || o.mfma_tile_rows % 16)
     return set_error(PSA_ERR_INVALID_ARGUMENT, "mfma_tile_rows must be a multiple of 16 in [16, 128]");
@@ -99,7 +101,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   const int64_t n_qpages = N > 0 ? b->query_page_off[N] : 0;
   if (n_gpages > 0 && !b->group_pages) return set_error(PSA_ERR_INVALID_ARGUMENT, "group_pages is NULL");
   if (n_qpages > 0 && !b->query_pages) return set_error(PSA_ERR_INVALID_ARGUMENT, "query_pages is NULL");
-  if (n_gpages > INT32_MAX || n_qpages > INT32_MAX)
+  if (n_gpages + n_qpages > INT32_MAX)
     return set_error(PSA_ERR_UNSUPPORTED, "page tables longer than 2^31 entries");
   for (int g = 0; g < G; ++g) {
     psa_status s = check_segment("group", g, b->group_prefix_len[g], b->group_page_off[g], b->group_page_off[g + 1],
@@ -140,14 +142,24 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
       if (b->query_group[i] >= 0) members[fill[b->query_group[i]]++] = i;
   }
 
-  // partial counts per query: prefix chunks first, then distinct chunks
+  // prefix tiling per group: MFMA tiles (bf16, enough rows) take chunks of
+  // up to prefix_chunk_tokens; small groups fall back to per-query mat-vec
+  // tiles whose chunks hold at most kMaxMatvecPages pages
   const int64_t Cp = o.prefix_chunk_tokens, Cd = o.distinct_chunk_tokens;
+  std::vector<char> group_mfma(G, 0);
+  std::vector<int64_t> group_chunk(G, Cp);
+  for (int g = 0; g < G; ++g) {
+    const int64_t rows = (int64_t)(member_off[g + 1] - member_off[g]) * r;
+    group_mfma[g] = bf16 && !(o.flags & PSA_PLAN_FORCE_MATVEC) && rows >= o.mfma_min_rows;
+    if (!group_mfma[g]) group_chunk[g] = std::min<int64_t>(Cp, kMaxMatvecPages * 16);
+  }
+  // partial counts per query: prefix chunks first, then distinct chunks
   std::vector<int32_t> n_pc(N, 0), expected(N, 0), slot_off(N, -1);
   int64_t slots = 0;
   for (int i = 0; i < N; ++i) {
     const int g = b->query_group[i];
     const int64_t lp = g >= 0 ? b->group_prefix_len[g] : 0;
-    n_pc[i] = use_prefix ? (int32_t)ceil_div(lp, Cp) : 0;
+    n_pc[i] = use_prefix && g >= 0 ? (int32_t)ceil_div(lp, group_chunk[g]) : 0;
     const int64_t n_dc = use_distinct ? ceil_div(b->query_distinct_len[i], Cd) : 0;
     expected[i] = n_pc[i] + (int32_t)n_dc;
     if (expected[i] >= 2) {
@@ -161,16 +173,17 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   }
 
   // ---- work items with a cost estimate (arbitrary time units) ----
+  // MFMA tiles fill a whole workgroup; mat-vec and empty items are wave-level
+  // and are packed four to a workgroup (unit).
   struct Cand {
     WorkItem it;
     double cost;
-    int64_t set;  // items of one set share a prefix chunk and go to one XCD
   };
-  std::vector<Cand> cands;
-  const double bw_slot = 8.0e3 / 512.0;   // bytes per ns per workgroup slot (HBM share)
-  const double mfma_slot = 2.5e6 / 512.0 * 0.5;  // flop per ns per workgroup slot at half rate
-  const double fixed = 300.0;             // per-item overhead, ns
-  int64_t set_id = 0;
+  std::vector<Cand> mfma, waves;
+  std::vector<int64_t> mfma_set;
+  const double bw_wave = 8.0e3 / 2048.0;          // bytes per ns per resident wave (HBM share)
+  const double mfma_slot = 2.5e6 / 512.0 * 0.5;   // flop per ns per workgroup slot at half rate
+  const double fixed = 300.0;                     // per-item overhead, ns
   int64_t n_prefix_items = 0, n_matvec_items = 0;
   const int64_t tile_max = o.mfma_tile_rows;
   for (int g = 0; g < G && use_prefix; ++g) {
@@ -178,29 +191,33 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     const int nm = member_off[g + 1] - member_off[g];
     if (lp == 0 || nm == 0) continue;
     const int64_t rows = (int64_t)nm * r;
-    const bool mfma = bf16 && !(o.flags & PSA_PLAN_FORCE_MATVEC) && rows >= o.mfma_min_rows;
-    const int64_t nchunks = ceil_div(lp, Cp);
+    const bool mf = group_mfma[g];
+    const int64_t C = group_chunk[g];
+    const int64_t nchunks = ceil_div(lp, C);
     for (int64_t ch = 0; ch < nchunks; ++ch) {
-      const int32_t tb = (int32_t)(ch * Cp), te = (int32_t)std::min(lp, (ch + 1) * Cp);
+      const int32_t tb = (int32_t)(ch * C), te = (int32_t)std::min(lp, (ch + 1) * C);
+      const int32_t pbase = (int32_t)(b->group_page_off[g] + tb / P);
       const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
-      if (mfma) {
+      if (mf) {
         const int64_t ntiles = ceil_div(rows, tile_max);
         const int64_t per = round_up(ceil_div(rows, ntiles), 16);
         for (int kvh = 0; kvh < hkv; ++kvh) {
           for (int64_t rb = 0; rb < rows; rb += per) {
             const int64_t rc = std::min(per, rows - rb);
-            WorkItem it{ITEM_PREFIX_MFMA, kvh, g, tb, te, (int32_t)rb, (int32_t)rc, (int32_t)ch};
+            WorkItem it{(int32_t)(ITEM_PREFIX_MFMA | (ch << 8)), kvh, g, tb, te, pbase, (int32_t)rb, (int32_t)rc};
             const double fl = (double)round_up(te - tb, 64) * round_up(rc, 16) * d * 4;
-            cands.push_back({it, fixed + std::max(fl / mfma_slot, kv_bytes / bw_slot), set_id});
+            mfma.push_back({it, fixed + std::max(fl / mfma_slot, 4.0 * kv_bytes / bw_wave)});
+            mfma_set.push_back(((int64_t)g * nchunks + ch) * hkv + kvh);
             ++n_prefix_items;
           }
-          ++set_id;
         }
       } else {
         for (int t = member_off[g]; t < member_off[g + 1]; ++t) {
+          const int qi = members[t];
           for (int kvh = 0; kvh < hkv; ++kvh) {
-            WorkItem it{ITEM_MATVEC_PREFIX, kvh, members[t], tb, te, 0, 0, (int32_t)ch};
-            cands.push_back({it, fixed + kv_bytes / bw_slot, set_id++});
+            const int32_t slot = expected[qi] >= 2 ? (int32_t)(((int64_t)slot_off[qi] + ch) * hkv + kvh) : -1;
+            WorkItem it{ITEM_MATVEC, kvh, qi, tb, te, pbase, expected[qi], slot};
+            waves.push_back({it, fixed + kv_bytes / bw_wave});
             ++n_matvec_items;
           }
         }
@@ -212,34 +229,59 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     const int64_t nchunks = ceil_div(ld, Cd);
     for (int64_t ch = 0; ch < nchunks; ++ch) {
       const int32_t tb = (int32_t)(ch * Cd), te = (int32_t)std::min(ld, (ch + 1) * Cd);
+      const int32_t pbase = (int32_t)(n_gpages + b->query_page_off[i] + tb / P);
       const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
       for (int kvh = 0; kvh < hkv; ++kvh) {
-        WorkItem it{ITEM_MATVEC_DISTINCT, kvh, i, tb, te, 0, 0, (int32_t)(n_pc[i] + ch)};
-        cands.push_back({it, fixed + kv_bytes / bw_slot, set_id++});
+        const int32_t slot =
+            expected[i] >= 2 ? (int32_t)(((int64_t)slot_off[i] + n_pc[i] + ch) * hkv + kvh) : -1;
+        WorkItem it{ITEM_MATVEC, kvh, i, tb, te, pbase, expected[i], slot};
+        waves.push_back({it, fixed + kv_bytes / bw_wave});
         ++n_matvec_items;
       }
     }
   }
   for (int i = 0; i < N; ++i) {
     if (expected[i] == 0) {  // only under PREFIX_ONLY / DISTINCT_ONLY
-      WorkItem it{ITEM_EMPTY, 0, i, 0, 0, 0, 0, 0};
-      cands.push_back({it, 1.0, set_id++});
+      WorkItem it{ITEM_EMPTY, 0, i, 0, 0, 0, 0, -1};
+      waves.push_back({it, 1.0});
     }
+  }
+
+  // ---- units: one MFMA tile, or four wave items of similar cost ----
+  struct Unit {
+    WorkItem it[kUnitItems];
+    double cost;
+    int64_t set;  // units of one set re-read one prefix chunk: same XCD
+  };
+  std::vector<Unit> units;
+  const WorkItem nop{ITEM_NOP, 0, 0, 0, 0, 0, 0, -1};
+  for (size_t t = 0; t < mfma.size(); ++t) {
+    Unit u{{mfma[t].it, nop, nop, nop}, mfma[t].cost, mfma_set[t]};
+    units.push_back(u);
+  }
+  std::stable_sort(waves.begin(), waves.end(), [](const Cand& a, const Cand& b2) { return a.cost > b2.cost; });
+  int64_t next_set = (int64_t)mfma.size() + 1 + (mfma_set.empty() ? 0 : *std::max_element(mfma_set.begin(), mfma_set.end()));
+  for (size_t t = 0; t < waves.size(); t += kUnitItems) {
+    Unit u{{nop, nop, nop, nop}, 0.0, next_set++};
+    for (int w = 0; w < kUnitItems && t + w < waves.size(); ++w) {
+      u.it[w] = waves[t + w].it;
+      u.cost = std::max(u.cost, waves[t + w].cost);
+    }
+    units.push_back(u);
   }
 
   // ---- ordering: longest first; sets spread over 8 XCD queues (workgroup
   // i runs on XCD i % 8), so tiles re-reading one prefix chunk share an L2 ----
-  std::vector<WorkItem> items;
-  items.reserve(cands.size());
+  std::vector<Unit> ordered;
+  ordered.reserve(units.size());
   if (o.flags & PSA_PLAN_NO_XCD_ORDER) {
-    std::stable_sort(cands.begin(), cands.end(), [](const Cand& a, const Cand& b2) { return a.cost > b2.cost; });
-    for (auto& x : cands) items.push_back(x.it);
+    std::stable_sort(units.begin(), units.end(), [](const Unit& a, const Unit& b2) { return a.cost > b2.cost; });
+    ordered = units;
   } else {
-    // group candidates by set
-    std::vector<int64_t> order(cands.size());
+    std::vector<int64_t> order(units.size());
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b2) {
-      if (cands[a].set != cands[b2].set) return cands[a].set < cands[b2].set;
+      if (units[a].set != units[b2].set) return units[a].set < units[b2].set;
       return a < b2;
     });
     struct Set {
@@ -250,7 +292,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     for (size_t t = 0; t < order.size();) {
       size_t u = t;
       double cs = 0;
-      while (u < order.size() && cands[order[u]].set == cands[order[t]].set) cs += cands[order[u++]].cost;
+      while (u < order.size() && units[order[u]].set == units[order[t]].set) cs += units[order[u++]].cost;
       sets.push_back({(int64_t)t, (int64_t)u, cs});
       t = u;
     }
@@ -266,17 +308,21 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
       load[best] += s.cost;
     }
     for (auto& qq : q)
-      std::stable_sort(qq.begin(), qq.end(), [&](int64_t a, int64_t b2) { return cands[a].cost > cands[b2].cost; });
+      std::stable_sort(qq.begin(), qq.end(), [&](int64_t a, int64_t b2) { return units[a].cost > units[b2].cost; });
     size_t longest = 0;
     for (auto& qq : q) longest = std::max(longest, qq.size());
     for (size_t k = 0; k < longest; ++k)
       for (int x = 0; x < kXcd; ++x)
-        if (k < q[x].size()) items.push_back(cands[q[x][k]].it);
+        if (k < q[x].size()) ordered.push_back(units[q[x][k]]);
   }
-  if (items.size() > (size_t)INT32_MAX) {
+  if (ordered.size() > (size_t)INT32_MAX / kUnitItems) {
     delete plan;
     return set_error(PSA_ERR_UNSUPPORTED, "work list too long");
   }
+  std::vector<WorkItem> items;
+  items.reserve(ordered.size() * kUnitItems);
+  for (const Unit& u : ordered)
+    for (int w = 0; w < kUnitItems; ++w) items.push_back(u.it[w]);
 
   // ---- workspace image ----
   ImageLayout L{};
@@ -287,23 +333,25 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     return at;
   };
   L.items = sect((int64_t)items.size() * (int64_t)sizeof(WorkItem));
-  L.group_page_off = sect((G + 1) * 4);
-  L.group_pages = sect(n_gpages * 4);
-  L.group_len = sect(G * 4);
+  L.pages = sect((n_gpages + n_qpages) * 4);
   L.member_off = sect((G + 1) * 4);
   L.members = sect((int64_t)members.size() * 4);
-  L.query_page_off = sect((N + 1) * 4);
-  L.query_pages = sect(n_qpages * 4);
-  L.query_group = sect(N * 4);
-  L.query_dlen = sect(N * 4);
   L.expected = sect(N * 4);
   L.slot_off = sect(N * 4);
   L.counters = sect((int64_t)N * hkv * 4);
   L.meta_bytes = off;
-  L.part_o = sect(slots * hkv * r * d * 4);
-  L.part_ml = sect(slots * hkv * r * 2 * 4);
+  const int64_t part_o_bytes = slots * hkv * r * d * 4;
+  const int64_t part_ml_bytes = slots * hkv * r * 2 * 4;
+  if (part_o_bytes >= (int64_t)UINT32_MAX) {
+    delete plan;
+    return set_error(PSA_ERR_UNSUPPORTED, "partial results exceed 4 GiB; use larger chunks");
+  }
+  L.part_o = sect(part_o_bytes);
+  L.part_ml = sect(part_ml_bytes);
   L.total_bytes = off;
   plan->layout = L;
+  plan->part_o_bytes = (uint32_t)part_o_bytes;
+  plan->part_ml_bytes = (uint32_t)part_ml_bytes;
 
   std::vector<uint8_t>& img = plan->image;
   try {
@@ -317,27 +365,22 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     std::memcpy(img.data() + at + idx * 4, &x, 4);
   };
   if (!items.empty()) std::memcpy(img.data() + L.items, items.data(), items.size() * sizeof(WorkItem));
-  for (int g = 0; g <= G && G > 0; ++g) put32(L.group_page_off, g, b->group_page_off[g]);
-  if (G == 0) put32(L.group_page_off, 0, 0);
-  for (int64_t t = 0; t < n_gpages; ++t) put32(L.group_pages, t, b->group_pages[t]);
-  for (int g = 0; g < G; ++g) put32(L.group_len, g, b->group_prefix_len[g]);
+  for (int64_t t = 0; t < n_gpages; ++t) put32(L.pages, t, b->group_pages[t]);
+  for (int64_t t = 0; t < n_qpages; ++t) put32(L.pages, n_gpages + t, b->query_pages[t]);
   for (int g = 0; g <= G; ++g) put32(L.member_off, g, member_off[g]);
   for (size_t t = 0; t < members.size(); ++t) put32(L.members, t, members[t]);
-  for (int i = 0; i <= N && N > 0; ++i) put32(L.query_page_off, i, b->query_page_off[i]);
-  if (N == 0) put32(L.query_page_off, 0, 0);
-  for (int64_t t = 0; t < n_qpages; ++t) put32(L.query_pages, t, b->query_pages[t]);
   for (int i = 0; i < N; ++i) {
-    put32(L.query_group, i, b->query_group[i]);
-    put32(L.query_dlen, i, b->query_distinct_len[i]);
     put32(L.expected, i, expected[i]);
     put32(L.slot_off, i, slot_off[i]);
   }
   // counters stay zero
+  plan->num_units = (int64_t)ordered.size();
+  plan->num_group_pages = n_gpages;
 
   // ---- statistics ----
   psa_plan_info& info = plan->info;
   info.workspace_bytes = (size_t)L.total_bytes;
-  info.num_items = (int64_t)items.size();
+  info.num_items = plan->num_units;
   info.num_prefix_items = n_prefix_items;
   info.num_matvec_items = n_matvec_items;
   info.num_partial_slots = slots * hkv;

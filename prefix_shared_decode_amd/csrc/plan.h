@@ -17,7 +17,10 @@ struct psa_plan {
   psa_plan_info info{};
   psa::ImageLayout layout{};
   std::vector<uint8_t> image;          // bytes [0, layout.meta_bytes) of the workspace
-  std::vector<psa::WorkItem> items;    // host copy of the work list (tests)
+  std::vector<psa::WorkItem> items;    // host copy of the work list (tests), 4 per unit
+  int64_t num_units = 0;               // workgroups of the fused launch
+  int64_t num_group_pages = 0;         // query pages follow the group pages in the page array
+  uint32_t part_o_bytes = 0, part_ml_bytes = 0;
   std::vector<int32_t> expected;       // per query
   std::vector<int32_t> slot_off;       // per query (-1: written directly)
   // pinned staging buffer for the upload, allocated on first upload

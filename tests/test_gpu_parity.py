@@ -253,3 +253,25 @@ def test_full_size_sampled(name):
     assert_close(got, O, "bf16", f"full {name} sampled")
     assert np.abs((gm + np.log(gl)) - (M + np.log(L))).max() <= 2e-4
     assert torch.isfinite(out).all()
+
+
+def test_late_dominant_key_triggers_exact_rescaling():
+    """A key far above everything before it, late in a chunk: the mat-vec tile's
+    fixed reference max is exceeded and the tile redoes the chunk; the MFMA
+    tile rescales its accumulators.  Either way the result is the plain softmax."""
+    import torch
+
+    wl = build_single_level("late_key", 32, 8, 128, "bf16", [(400, 6, (0, 30))], (3, (200, 300)), seed=13)
+    q, k, v = values(wl)
+    b = wl.batch
+    r = 4
+    # ungrouped query 6: dominant key at its distinct token 250 for kv head 1
+    i = 6
+    pages = b["query_pages"][b["query_page_off"][i]:b["query_page_off"][i + 1]]
+    t = 250 if b["query_distinct_len"][i] > 250 else int(b["query_distinct_len"][i]) - 1
+    k[int(pages[t // 16]), 1, t % 16, :] = (12.0 * q[i, 1 * r, :].float()).to(torch.bfloat16)
+    # group 0: dominant key at prefix token 380 for kv head 2
+    gp = b["group_pages"][b["group_page_off"][0]:b["group_page_off"][1]]
+    k[int(gp[380 // 16]), 2, 380 % 16, :] = (12.0 * q[0, 2 * r, :].float()).to(torch.bfloat16)
+    _check_full(wl, b, q, k, v, "late dominant key")
+    _check_full(wl, b, q, k, v, "late dominant key, mat-vec only", flags=P.FORCE_MATVEC)

@@ -51,24 +51,45 @@ def _cfg(wl, **kw):
 
 
 def _coverage(wl, plan):
-    """Expand the work list to (query, kv head) -> list of (segment, tok_begin, tok_end, slot)."""
+    """Expand the work list to (query, kv head) -> list of (segment, tok_begin, tok_end, slot j)."""
     b = wl.batch
     r = wl.num_q_heads // wl.num_kv_heads
+    n_gpages = len(b["group_pages"])
+    _, slot_off = plan.queries()
     cov = {}
     members = {}
     for i, g in enumerate(b["query_group"]):
         if g >= 0:
             members.setdefault(int(g), []).append(i)
-    for kind, kvh, ident, tb, te, rb, rc, slot in plan.items():
-        if kind in (0, 1):
-            cov.setdefault((ident, kvh), []).append(("d" if kind == 0 else "p", tb, te, slot))
+    items = plan.items()
+    assert len(items) % 4 == 0
+    for u in range(len(items) // 4):
+        unit = items[4 * u: 4 * u + 4]
+        if unit[0][0] & 0xFF == 2:
+            assert all(x[0] == 0 for x in unit[1:]), "an MFMA tile fills its unit"
+    for kind_full, kvh, ident, tb, te, pbase, a, bb in items:
+        kind = kind_full & 0xFF
+        if kind == 1:
+            seg = "p" if pbase < n_gpages else "d"
+            if seg == "p":
+                g = int(b["query_group"][ident])
+                assert pbase == b["group_page_off"][g] + tb // 16
+            else:
+                assert pbase == n_gpages + b["query_page_off"][ident] + tb // 16
+            j = bb // wl.num_kv_heads - slot_off[ident] if bb >= 0 else 0
+            if bb >= 0:
+                assert bb % wl.num_kv_heads == kvh
+            cov.setdefault((ident, kvh), []).append((seg, tb, te, j, a))
         elif kind == 2:
-            assert rb % r == 0 and rc % r == 0 and 0 < rc <= 128
-            for mi in range(rb // r, (rb + rc) // r):
-                cov.setdefault((members[ident][mi], kvh), []).append(("p", tb, te, slot))
+            assert a % r == 0 and bb % r == 0 and 0 < bb <= 128
+            assert pbase == b["group_page_off"][ident] + tb // 16
+            for mi in range(a // r, (a + bb) // r):
+                cov.setdefault((members[ident][mi], kvh), []).append(("p", tb, te, kind_full >> 8, None))
         elif kind == 3:
             for kvh2 in range(wl.num_kv_heads):
-                cov.setdefault((ident, kvh2), []).append(("e", 0, 0, 0))
+                cov.setdefault((ident, kvh2), []).append(("e", 0, 0, 0, None))
+        else:
+            assert kind == 0
     return cov
 
 
@@ -85,7 +106,7 @@ def _check_coverage(wl, plan, prefix=True, distinct=True):
             want_p = set(range(lp)) if prefix else set()
             want_d = set(range(ld)) if distinct else set()
             got_p, got_d = [], []
-            for seg, tb, te, _ in parts:
+            for seg, tb, te, _, _ in parts:
                 assert tb % 16 == 0
                 (got_p if seg == "p" else got_d if seg == "d" else []).extend(range(tb, te))
             assert sorted(got_p) == sorted(want_p)
@@ -95,6 +116,7 @@ def _check_coverage(wl, plan, prefix=True, distinct=True):
             if not real:
                 assert any(x[0] == "e" for x in parts)
             assert sorted(x[3] for x in real) == list(range(len(real)))
+            assert all(x[4] is None or x[4] == expected[i] for x in real)
             # prefix partials come first
             assert all(x[3] < sum(1 for y in real if y[0] == "p") for x in real if x[0] == "p")
             assert (slot_off[i] >= 0) == (expected[i] >= 2)
@@ -129,7 +151,7 @@ def test_mfma_tiles_only_for_bf16_groups_with_enough_rows():
     assert plan.info()["num_prefix_items"] == 0
     plan = P.psa_build_plan(_cfg(wl), wl.batch, mfma_min_rows=8)
     it = plan.items()
-    assert set(it[it[:, 0] == 2][:, 2]) == {1}
+    assert set(it[(it[:, 0] & 0xFF) == 2][:, 2]) == {1}
     wl32 = build_single_level("t", 4, 2, 128, "f32", [(64, 30, (1, 5))], [], seed=1)
     assert P.psa_build_plan(_cfg(wl32), wl32.batch).info()["num_prefix_items"] == 0
 
@@ -139,15 +161,20 @@ def test_xcd_order_keeps_prefix_sets_on_one_xcd():
     plan = P.psa_build_plan(_cfg(wl), wl.batch)
     it = plan.items()
     pos = {}
-    for idx, row in enumerate(it):
-        if row[0] == 2:
-            pos.setdefault((row[2], row[1], row[3]), []).append(idx)
+    for idx in range(0, len(it), 4):
+        row = it[idx]
+        if row[0] & 0xFF == 2:
+            pos.setdefault((row[2], row[1], row[0] >> 8), []).append(idx // 4)
+    # 8 groups x 8 kv heads x 1 prefix chunk, each set = 4 row tiles
     assert len(pos) == 64 and all(len(v) == 4 for v in pos.values())
     for v in pos.values():
         assert len({x % 8 for x in v}) == 1
-    # longest-first within the list: all MFMA tiles come before mat-vec tiles
-    kinds = it[:, 0]
-    assert kinds[: 256].tolist() == [2] * 256
+    # longest first: all MFMA units come before the mat-vec units
+    kinds = it[::4, 0] & 0xFF
+    assert kinds[:256].tolist() == [2] * 256 and set(kinds[256:].tolist()) == {1}
+    # a smaller explicit chunk splits each set's prefix
+    it = P.psa_build_plan(_cfg(wl), wl.batch, prefix_chunk_tokens=1024).items()
+    assert ((it[::4, 0] & 0xFF) == 2).sum() == 512
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32_1x4", "llama3_8b_8x100", "longchat13b_1x256", "no_sharing_512"])
@@ -203,6 +230,8 @@ def test_error_paths():
     assert _status(lambda: mk(flags=P.PREFIX_ONLY | P.DISTINCT_ONLY)) == "PSA_ERR_INVALID_ARGUMENT"
     assert _status(lambda: mk(prefix_chunk_tokens=20)) == "PSA_ERR_INVALID_ARGUMENT"
     assert _status(lambda: mk(mfma_tile_rows=256)) == "PSA_ERR_INVALID_ARGUMENT"
+    assert _status(lambda: mk(prefix_chunk_tokens=4096)) == "PSA_ERR_INVALID_ARGUMENT"
+    assert _status(lambda: mk(distinct_chunk_tokens=2048)) == "PSA_ERR_INVALID_ARGUMENT"
     assert _status(lambda: mk(flags=0x400)) == "PSA_ERR_INVALID_ARGUMENT"
     # messages name the problem
     with pytest.raises(P.PsaError, match="page id"):
