@@ -6,8 +6,9 @@ workload (default: Llama-3-8B attention shape, 8 prefix groups x 100
 requests, 2048-token prefixes, distinct lengths U[64, 512], bf16), with Q and
 the paged K/V pools already resident in HBM.  The plan is built and uploaded
 before timing.  Each timed step is bracketed by HIP events on the launch
-stream; L2 and the 256 MB MALL are flushed (1 GiB write) before every step,
-outside the events.  Prints one JSON line.
+stream; L2 and the 256 MB MALL are flushed before every step, outside the
+events, by reading a 1 GiB buffer (a read leaves no dirty lines whose
+write-back would be charged to the timed launch).  Prints one JSON line.
 
 --gpus N with N > 1 is refused: this build measures one GPU.
 """
@@ -132,6 +133,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_8b_8x100")
     ap.add_argument("--no-flush", action="store_true", help="do not flush L2/MALL between steps")
+    ap.add_argument("--write-flush", action="store_true",
+                    help="flush by writing 1 GiB (leaves dirty lines) instead of reading it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--flags", type=int, default=0, help="psa_plan flags (e.g. 1 = PREFIX_ONLY)")
@@ -182,7 +185,8 @@ def main():
     def step():
         P.psa_decode_attention(plan, q, k, v, out, ws)
 
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
     if args.copy_calib_mib > 0:
         # a plain copy kernel of known size: reads and writes exactly this many bytes
         src = torch.ones(args.copy_calib_mib << 20, dtype=torch.uint8, device="cuda")
@@ -199,7 +203,10 @@ def main():
     t_wall = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            if args.write_flush:
+                flush.fill_(float(i))
+            else:
+                torch.sum(flush, dim=None, out=sink)
         evs[i][0].record()
         step()
         evs[i][1].record()
