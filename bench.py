@@ -126,6 +126,51 @@ def cpu_baseline(wl, batch, q, k, v, target_s, max_s):
     }
 
 
+def trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, path):
+    """One traced launch (after a cache flush): per-kind unit durations and a
+    timeline of how many units of each kind run at once (10 us bins)."""
+    import numpy as np
+    import torch
+
+    units = int(info["num_items"])
+    tr = torch.zeros(units * 4, dtype=torch.int64, device="cuda")
+    if flush is not None:
+        torch.sum(flush, dim=None, out=sink)
+    P.psa_decode_attention(plan, q, k, v, out, ws, trace=tr)
+    torch.cuda.synchronize()
+    t = tr.view(units, 4).cpu().numpy()
+    ok = (t[:, 0] > 0) & (t[:, 1] >= t[:, 0])
+    if not ok.all():
+        log(f"trace: {int((~ok).sum())} of {units} units without a valid record, e.g. {t[~ok][:3].tolist()}")
+        t = t[ok]
+    if len(t) == 0:
+        return
+    t0 = t[:, 0].min()
+    start = (t[:, 0] - t0) / 100.0  # 100 MHz clock -> us
+    end = (t[:, 1] - t0) / 100.0
+    kind = t[:, 3]
+    names = {0: "nop", 1: "matvec", 2: "mfma_prefix", 3: "empty"}
+    res = {"units": units, "span_us": float(end.max()), "kinds": {}}
+    bins = np.arange(0.0, float(end.max()) + 10.0, 10.0)
+    for kd in np.unique(kind):
+        sel = kind == kd
+        dur = end[sel] - start[sel]
+        active = [int(((start[sel] < b + 10.0) & (end[sel] > b)).sum()) for b in bins]
+        res["kinds"][names.get(int(kd), str(kd))] = {
+            "count": int(sel.sum()), "dur_us_mean": float(dur.mean()), "dur_us_p50": float(np.median(dur)),
+            "dur_us_max": float(dur.max()), "first_start_us": float(start[sel].min()),
+            "last_start_us": float(start[sel].max()), "last_end_us": float(end[sel].max()),
+            "active_per_10us": active}
+    xcc = (t[:, 2] >> 32) & 0xF
+    res["units_per_xcc"] = [int((xcc == x).sum()) for x in range(8)]
+    with open(path, "w") as f:
+        json.dump(res, f)
+    for name, r in res["kinds"].items():
+        log(f"trace {name}: n={r['count']} dur mean {r['dur_us_mean']:.1f} us max {r['dur_us_max']:.1f}, "
+            f"starts {r['first_start_us']:.1f}..{r['last_start_us']:.1f}, last end {r['last_end_us']:.1f} us")
+    log(f"trace span {res['span_us']:.1f} us")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +187,8 @@ def main():
     ap.add_argument("--distinct-chunk", type=int, default=0)
     ap.add_argument("--tile-rows", type=int, default=0)
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--trace", default=None,
+                    help="after timing, run one traced launch and write its per-unit timeline summary (JSON) here")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (counter calibration)")
     args = ap.parse_args()
@@ -259,6 +306,8 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle on a sample")
         rec["cpu_baseline"] = cpu_baseline(wl, batch, q, k, v, args.cpu_seconds, 30.0)
+    if args.trace:
+        trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, args.trace)
     line = json.dumps(rec)
     print(line, flush=True)
     if args.json_out:

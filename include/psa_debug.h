@@ -26,6 +26,18 @@ psa_status psa_plan_debug_items(const psa_plan* plan, int32_t* out, int64_t capa
  * tile writes it directly) and its first partial slot (-1 if none). */
 psa_status psa_plan_debug_queries(const psa_plan* plan, int32_t* expected, int32_t* slot_off, int64_t capacity);
 
+/* psa_decode_attention that also records, per unit (workgroup) of the fused
+ * launch, 4 uint64 to device memory d_trace: start and end time of the
+ * workgroup (the GPU's constant 100 MHz clock), the HW_ID register (CU, SIMD,
+ * shader engine) | XCC_ID << 32, and the unit's kind (1 mat-vec, 2 MFMA
+ * prefix tile, 3 empty, 0 nothing).  trace_capacity (entries) must be >=
+ * 4 * num_items.  Each workgroup ends with one extra barrier; results are the
+ * same as psa_decode_attention's. */
+psa_status psa_decode_attention_traced(const psa_plan* plan, const void* d_q, const void* d_k_pool,
+                                       const void* d_v_pool, void* d_out, float* d_out_m, float* d_out_l,
+                                       void* d_workspace, size_t bytes, void* d_trace, int64_t trace_capacity,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

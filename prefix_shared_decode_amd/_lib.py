@@ -24,7 +24,8 @@ STATUS = {0: "PSA_OK", 1: "PSA_ERR_INVALID_ARGUMENT", 2: "PSA_ERR_UNSUPPORTED", 
 # every symbol include/psa.h and include/psa_debug.h declare
 EXPORTS = ["psa_build_plan", "psa_plan_get_info", "psa_plan_upload", "psa_decode_attention", "psa_merge",
            "psa_flatten_prefix_tree", "psa_batch_owned_view", "psa_free_batch", "psa_destroy_plan",
-           "psa_last_error", "psa_version", "psa_plan_debug_items", "psa_plan_debug_queries"]
+           "psa_last_error", "psa_version", "psa_plan_debug_items", "psa_plan_debug_queries",
+           "psa_decode_attention_traced"]
 
 
 class PsaError(RuntimeError):
@@ -100,6 +101,7 @@ def lib():
         L.psa_version.restype = C.c_int32
         L.psa_plan_debug_items.argtypes = [vp, _I32P, C.c_int64]
         L.psa_plan_debug_queries.argtypes = [vp, _I32P, _I32P, C.c_int64]
+        L.psa_decode_attention_traced.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp, C.c_int64, vp]
         for name in EXPORTS:
             fn = getattr(L, name)
             if fn.restype is C.c_int and name not in ("psa_version",):
@@ -234,8 +236,12 @@ def psa_plan_upload(plan, workspace, stream=None):
                                  workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
 
 
-def psa_decode_attention(plan, q, k_pool, v_pool, out, workspace, out_m=None, out_l=None, stream=None):
-    """One fused decode launch; shapes/dtypes are checked against the plan's config."""
+def psa_decode_attention(plan, q, k_pool, v_pool, out, workspace, out_m=None, out_l=None, stream=None, trace=None):
+    """One fused decode launch; shapes/dtypes are checked against the plan's config.
+
+    trace: optional int64 device tensor of >= 4 * num_items entries; the launch
+    then records per-unit timing (include/psa_debug.h psa_decode_attention_traced).
+    """
     import torch
 
     cfg = plan.cfg
@@ -251,10 +257,15 @@ def psa_decode_attention(plan, q, k_pool, v_pool, out, workspace, out_m=None, ou
     for name, t in (("out_m", out_m), ("out_l", out_l)):
         if t is not None and (tuple(t.shape) != (n, cfg.num_q_heads) or t.dtype != torch.float32):
             raise ValueError(f"{name}: expected {(n, cfg.num_q_heads)} float32")
-    _check(lib().psa_decode_attention(plan.handle, _dev_ptr(q, "q"), _dev_ptr(k_pool, "k_pool"),
-                                      _dev_ptr(v_pool, "v_pool"), _dev_ptr(out, "out"), _dev_ptr(out_m, "out_m"),
-                                      _dev_ptr(out_l, "out_l"), _dev_ptr(workspace, "workspace"),
-                                      workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    args = (plan.handle, _dev_ptr(q, "q"), _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"),
+            _dev_ptr(out, "out"), _dev_ptr(out_m, "out_m"), _dev_ptr(out_l, "out_l"),
+            _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size())
+    if trace is None:
+        _check(lib().psa_decode_attention(*args, _stream_ptr(stream)))
+    else:
+        if trace.dtype != torch.int64:
+            raise ValueError("trace: expected an int64 tensor")
+        _check(lib().psa_decode_attention_traced(*args, _dev_ptr(trace, "trace"), trace.numel(), _stream_ptr(stream)))
 
 
 def psa_merge(o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, stream=None):

@@ -118,9 +118,9 @@ psa_status psa_plan_upload(psa_plan* plan, void* d_workspace, size_t bytes, void
   return PSA_OK;
 }
 
-psa_status psa_decode_attention(const psa_plan* plan, const void* d_q, const void* d_k_pool, const void* d_v_pool,
-                                void* d_out, float* d_out_m, float* d_out_l, void* d_workspace, size_t bytes,
-                                void* stream) {
+static psa_status decode_impl(const psa_plan* plan, const void* d_q, const void* d_k_pool, const void* d_v_pool,
+                              void* d_out, float* d_out_m, float* d_out_l, void* d_workspace, size_t bytes,
+                              uint64_t* d_trace, void* stream) {
   if (!plan) return set_error(PSA_ERR_INVALID_ARGUMENT, "plan is NULL");
   const psa::ImageLayout& L = plan->layout;
   if (bytes < (size_t)L.total_bytes)
@@ -173,10 +173,37 @@ psa_status psa_decode_attention(const psa_plan* plan, const void* d_q, const voi
   p.hkv = plan->cfg.num_kv_heads;
   p.scale_log2 = plan->sm_scale * 1.4426950408889634f;
   p.out_bf16 = plan->cfg.out_dtype == PSA_BF16;
+  p.trace = d_trace;
   e = psa::launch_decode(p, plan->cfg.head_dim, plan->r, plan->cfg.kv_dtype == PSA_BF16,
                          reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return psa::hip_fail(e, "decode kernel launch");
   return PSA_OK;
+}
+
+psa_status psa_decode_attention(const psa_plan* plan, const void* d_q, const void* d_k_pool, const void* d_v_pool,
+                                void* d_out, float* d_out_m, float* d_out_l, void* d_workspace, size_t bytes,
+                                void* stream) {
+  return decode_impl(plan, d_q, d_k_pool, d_v_pool, d_out, d_out_m, d_out_l, d_workspace, bytes, nullptr, stream);
+}
+
+psa_status psa_decode_attention_traced(const psa_plan* plan, const void* d_q, const void* d_k_pool,
+                                       const void* d_v_pool, void* d_out, float* d_out_m, float* d_out_l,
+                                       void* d_workspace, size_t bytes, void* d_trace, int64_t trace_capacity,
+                                       void* stream) {
+  if (!plan) return set_error(PSA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!d_trace) return set_error(PSA_ERR_INVALID_ARGUMENT, "trace is NULL");
+  if (trace_capacity < plan->num_units * 4)
+    return set_error(PSA_ERR_WORKSPACE_TOO_SMALL,
+                     "trace needs " + std::to_string(plan->num_units * 4) + " uint64 entries");
+  if (!plan->items.empty()) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return psa::hip_fail(e, "hipGetDevice");
+    psa_status s = psa::check_device_ptr(d_trace, "trace", dev);
+    if (s != PSA_OK) return s;
+  }
+  return decode_impl(plan, d_q, d_k_pool, d_v_pool, d_out, d_out_m, d_out_l, d_workspace, bytes,
+                     static_cast<uint64_t*>(d_trace), stream);
 }
 
 psa_status psa_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* m_a, const float* l_a,

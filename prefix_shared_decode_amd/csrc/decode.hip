@@ -24,6 +24,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "layout.h"
 #include "psa_internal.h"
@@ -71,7 +72,35 @@ __device__ __forceinline__ float sum8(float v) {
 }
 // Value of lane (i + 8) mod 16 within each row of 16 (row_ror:8) == lane i ^ 8.
 __device__ __forceinline__ float xor8(float v) { return dpp<0x128>(v); }
-__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+// A lane's value and that of lane ^ OFF (OFF = 8, 16 or 32), in an order that
+// depends on the lane; for symmetric combinations only.  8: row_ror:8 (DPP);
+// 16: v_permlane16_swap (odd and even rows of 16); 32: v_permlane32_swap.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float v, float& a, float& b) {
+  if constexpr (OFF == 8) {
+    a = v;
+    b = xor8(v);
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    static_assert(OFF == 32, "lane distance 8, 16 or 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
+// Max over the four lanes l, l^16, l^32, l^48 (in the MFMA tile: the lane
+// groups sharing one row): swap the 32-lane halves, then the odd and even
+// 16-lane rows.
+__device__ __forceinline__ float max_lane_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -324,8 +353,7 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
 #pragma unroll
           for (int t = 1; t < NT; ++t) mx = fmaxf(mx, s[t][h]);
           mx = fmaxf(mx, xor8(mx));
-          mx = fmaxf(mx, shfl_xor(mx, 16));
-          mx = fmaxf(mx, shfl_xor(mx, 32));  // page 0 always holds a valid token
+          mx = max_lane_groups(mx);  // page 0 always holds a valid token
           mref[h] = mx;
           mtrue[h] = -INFINITY;
         }
@@ -349,34 +377,39 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
     for (int h = 0; h < R; ++h) {
       float mx = mtrue[h];
       mx = fmaxf(mx, xor8(mx));
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
+      mx = max_lane_groups(mx);
       mref[h] = mx;
     }
     fixed_ref = true;
   }
 
-  // merge the token groups (lanes with equal lane % LPT)
-#pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
+  // merge the token groups (lanes with equal lane % LPT): a symmetric merge
+  // of each lane's state with its partner's at distance 8 (DPP), 16 and 32
+  // (permlane swaps), all in VALU
+  auto merge_step = [&](auto off_tag) {
+    constexpr int OFF = decltype(off_tag)::value;
 #pragma unroll
     for (int h = 0; h < R; ++h) {
-      const bool rot = off == 8;  // lane ^ 8 within a row of 16 is row_ror:8
-      const float mo = rot ? xor8(mref[h]) : shfl_xor(mref[h], off);
-      const float lo = rot ? xor8(l[h]) : shfl_xor(l[h], off);
-      const float mt = rot ? xor8(mtrue[h]) : shfl_xor(mtrue[h], off);
-      const float M = fmaxf(mref[h], mo);
-      const float a = fast_exp2(mref[h] - M), bw = fast_exp2(mo - M);
-      l[h] = l[h] * a + lo * bw;
+      float m0, m1, l0, l1, t0, t1;
+      lane_pair<OFF>(mref[h], m0, m1);
+      lane_pair<OFF>(l[h], l0, l1);
+      lane_pair<OFF>(mtrue[h], t0, t1);
+      const float M = fmaxf(m0, m1);
+      const float a = fast_exp2(m0 - M), bw = fast_exp2(m1 - M);
+      l[h] = l0 * a + l1 * bw;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
-        const float oo = rot ? xor8(o[h][e]) : shfl_xor(o[h][e], off);
-        o[h][e] = o[h][e] * a + oo * bw;
+        float o0, o1;
+        lane_pair<OFF>(o[h][e], o0, o1);
+        o[h][e] = o0 * a + o1 * bw;
       }
       mref[h] = M;
-      mtrue[h] = fmaxf(mtrue[h], mt);
+      mtrue[h] = fmaxf(t0, t1);
     }
-  }
+  };
+  if constexpr (LPT == 8) merge_step(std::integral_constant<int, 8>{});
+  merge_step(std::integral_constant<int, 16>{});
+  merge_step(std::integral_constant<int, 32>{});
 
   // lanes 0..LPT-1 write: O normalised, m (true max), l relative to it
   const int E = it.a, slot = it.b;
@@ -431,8 +464,9 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
 // Rows = (member query, head in kv group) pairs of one group, up to 128 rows
 // in 16-row slices (2 per wave), against one prefix chunk staged through LDS
 // 64 tokens (4 pages) at a time.  K and V are copied global -> LDS by the
-// load unit (global_load_lds_dwordx4, no registers), double buffered: block
-// b+1 is in flight while block b is computed.
+// load unit (global_load_lds_dwordx4, no registers), double buffered in two
+// separate LDS arrays: block b+1 is in flight while block b is computed.
+// Wave w copies page w of every 64-token block.
 //   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16: A = K rows (tokens), B = Q^T.
 //   O^T = V^T P^T with the same MFMA: A = V^T read from the row-major V tile
 //   with ds_read_b64_tr_b16 (transposing 4x16 bf16 blocks on the way), B = P^T.
@@ -451,7 +485,6 @@ struct MfShape {
   static constexpr int TILE = MfLayout<D>::TILE;
   static constexpr int NI = MfLayout<D>::NI;   // 1 KiB copies per wave per tile
   static constexpr int STAGE = 2 * TILE;       // K then V
-  static constexpr int LDS_BYTES = 2 * STAGE + kMaxPrefixChunk / 16 * 4 + 128 * 4 + 16;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -460,208 +493,288 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
 constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
+// Copy 16 bytes per lane from gbase + voff to LDS at lds + 16 * lane through
+// the load unit (global_load_lds_dwordx4, saddr form; M0 holds the LDS base
+// and is restored).  Written as inline asm so that the compiler does not make
+// every later LDS read wait for these copies: completion is awaited
+// explicitly with s_waitcnt vmcnt, followed by a barrier.  The LDS pointer is
+// an operand so that the compiler knows the stage may change.
+__device__ __forceinline__ void copy_to_lds(const char* gbase, uint32_t voff, lds_char* lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(gbase)
+      : "memory");
+}
+
+// Workgroup barrier ordering LDS accesses only (no wait for global memory,
+// so copies into the other stage stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+
+// Running state of a wave's NS row slices.
+template <int D>
+struct MfRows {
+  bf16x8 qb[2][D / 32];        // Q^T B operands
+  f32x4 o[2][D / 16];          // O^T accumulators (unnormalised, relative to mref)
+  f32x4 rsum[2];               // row sums of the bf16-rounded weights (every element)
+  float mref[2], mtrue[2];     // reference max (lazy) and true max, log2 units
+  float lrow[2];               // this lane's part of the row sum of exact weights
+};
+
+// One 64-token block (K at Ks, V at Vs) for the wave's NS slices; tokens at or
+// past `valid` are masked.
+template <int D, int NS>
+__device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, const lds_char* Vs, int valid, float sc,
+                                         const bf16x8& ones) {
+  constexpr int KK = D / 32, NB = D / 16;
+  // an opaque lane index: the LDS offsets derived from it are recomputed per
+  // block instead of being held in registers across the loop
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int l16 = lane & 15, lg = lane >> 4;
+  // ---- S^T tiles: t = kb*2 + half covers tokens 32kb + {8*(m/4) + 4*half + m%4} ----
+  f32x4 s[NS][4];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s[sl][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    bf16x8 a[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) a[kk] = *(const __attribute__((address_space(3))) bf16x8*)(Ks + mf_k_lds<D>(t, kk, lg, l16));
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) s[sl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], st.qb[sl][kk], s[sl][t], 0, 0, 0);
+  }
+  if (valid < 64) {  // last block of the chunk: mask tokens past its end
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((t >> 1) * 32 + 8 * lg + 4 * (t & 1) + i >= valid) s[sl][t][i] = -INFINITY;
+  }
+  // ---- online softmax per row (lane's row = l16; 16 raw scores per lane) ----
+  bf16x8 pb[NS][2];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[sl][t][i]);
+    mx = max_lane_groups(mx) * sc;  // log2 units (sc > 0 keeps the order)
+    st.mtrue[sl] = fmaxf(st.mtrue[sl], mx);
+    if (__builtin_amdgcn_ballot_w64(mx > st.mref[sl] + kLazy)) {
+      const float mn = fmaxf(st.mref[sl], mx);
+      const float alpha = fast_exp2(st.mref[sl] - mn);
+      st.mref[sl] = mn;
+      st.lrow[sl] *= alpha;
+      st.rsum[sl] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) st.o[sl][nb] *= alpha;
+    }
+    const float nm = -st.mref[sl];
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = fast_exp2(fmaf(s[sl][kb * 2][i], sc, nm));  // exp2(-inf) = 0 when masked
+        const float p1 = fast_exp2(fmaf(s[sl][kb * 2 + 1][i], sc, nm));
+        ps += p0 + p1;
+        v[i] = (__bf16)p0;
+        v[4 + i] = (__bf16)p1;
+      }
+      pb[sl][kb] = v;
+      // row sum of the bf16-rounded weights used in P.V, by MFMA against ones
+      st.rsum[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, v, st.rsum[sl], 0, 0, 0);
+    }
+    st.lrow[sl] += ps;
+  }
+  // ---- O^T += V^T P^T; V^T operand through transposing LDS reads ----
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      v4i16 h[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(Vs + mf_v_lds<D>(kb, nb, hf, lg, l16)));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) st.o[sl][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[sl][kb], st.o[sl][nb], 0, 0, 0);
+    }
+  }
+}
+
 template <int D, int R>
-__device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, char* smem) {
+__device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_char* stage0, lds_char* stage1,
+                                 int32_t* s_list, int* s_n) {
   using S = MfShape<D>;
   constexpr int KK = S::KK, NB = S::NB, NI = S::NI;
-  int32_t* s_pages = reinterpret_cast<int32_t*>(smem + 2 * S::STAGE);
-  int32_t* s_list = s_pages + kMaxPrefixChunk / 16;
-  int* s_n = s_list + 128;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int ROW = MfLayout<D>::ROW, TILEB = 16 * D * 2;  // bytes of one (page, kv head) tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   const int g = it.id, kvh = it.kvh, rb = it.a, rc = it.b, jslot = it.kind >> 8;
   const int ntok = it.tok_end - it.tok_begin, npages = (ntok + 15) >> 4, nblocks = (ntok + 63) >> 6;
   const int32_t* mem = p.members + p.member_off[g];
   const int nslices = (rc + 15) >> 4;
+  const int ns = wave + kWaves < nslices ? 2 : (wave < nslices ? 1 : 0);
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
   const char* kp = reinterpret_cast<const char*>(p.k);
   const char* vp = reinterpret_cast<const char*>(p.v);
 
-  for (int i = tid; i < npages; i += kThreads) s_pages[i] = p.pages[it.page_base + i];
+  // lane j holds the id of the page this wave copies in block j (page 4j+wave
+  // of the chunk, clamped to its last page); a chunk has at most 32 blocks
+  int pid_v = 0;
+  if (lane < nblocks) pid_v = p.pages[it.page_base + min(lane * 4 + wave, npages - 1)];
 
-  bool act[2];
-  bf16x8 qb[2][KK];
+  MfRows<D> st;
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
-    const int slice = wave + kWaves * sl;
-    const int row = slice * 16 + l16;
-    act[sl] = slice < nslices;
+    const int row = (wave + kWaves * sl) * 16 + l16;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (act[sl] && row < rc) {
+      if (sl < ns && row < rc) {
         const int grow = rb + row;
         const int qi = mem[grow / R];
         const int64_t off = ((int64_t)qi * p.hq + kvh * R + grow % R) * D + kk * 32 + lg * 8;
         w = *reinterpret_cast<const u32x4*>(qp + off);
       }
-      qb[sl][kk] = __builtin_bit_cast(bf16x8, w);
+      st.qb[sl][kk] = __builtin_bit_cast(bf16x8, w);
     }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) st.o[sl][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.rsum[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.mref[sl] = kNoMax;
+    st.mtrue[sl] = -INFINITY;
+    st.lrow[sl] = 0.f;
   }
-  f32x4 oacc[2][NB];
-#pragma unroll
-  for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) oacc[sl][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mref[2] = {kNoMax, kNoMax}, mtrue[2] = {-INFINITY, -INFINITY};
-  float lrow[2] = {0.f, 0.f};                  // per-lane part of the row sum of exact weights
-  f32x4 rsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // row sum of rounded weights
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
   const float sc = p.scale_log2;
-  __syncthreads();  // s_pages ready
+  // Use the loaded registers once here, so that the compiler waits for their
+  // loads before the block loop rather than at a first use inside it (a wait
+  // there would also wait for the copies in flight).
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(st.qb[sl][kk]));
+  asm volatile("" ::"v"(pid_v));
 
-  // copy of one 64-token block, global -> LDS through the load unit: wave w
-  // issues NI loads per tile, lane l writing 16 bytes (index maps in
-  // layout.h).  Tokens past the chunk re-read its last token so every LDS row
+  // copy of one 64-token block into a stage, global -> LDS through the load
+  // unit: this wave's NI loads per tile (index maps in layout.h) all fall in
+  // one page.  Tokens past the chunk re-read its last token so every LDS row
   // stays finite (their scores are masked).
-  const int64_t tile_stride = (int64_t)p.hkv * 16 * D * 2;
-  auto dma = [&](int blk, int stage) {
-    lds_char* kl = (lds_char*)(smem + stage * S::STAGE);
-    lds_char* vl = kl + S::TILE;
+  int tin[NI], coff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    tin[i] = mf_copy_token<D>(wave, i, lane) & 15;
+    coff[i] = mf_copy_chunk<D>(wave, i, lane) * 16;
+  }
+  const int64_t tile_stride = (int64_t)p.hkv * TILEB;
+  auto dma = [&](int blk, lds_char* stage) {
+    const int pg = min(blk * 4 + wave, npages - 1);
+    const int pid = __builtin_amdgcn_readlane(pid_v, blk);
+    const int du = (blk * 4 + wave - pg) * 16;  // > 0 only when this wave's page is past the chunk
+    const int lim = ntok - 1 - pg * 16;         // last valid token within the page
+    const int64_t tile = (int64_t)pid * tile_stride + (int64_t)kvh * TILEB;
+    const char* ks = kp + tile;
+    const char* vs = vp + tile;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int t = mf_copy_token<D>(wave, i, lane);
-      const int c = mf_copy_chunk<D>(wave, i, lane);
-      int tg = blk * 64 + t;
-      tg = tg < ntok ? tg : ntok - 1;
-      const int64_t off = (int64_t)s_pages[tg >> 4] * tile_stride + (int64_t)kvh * 16 * D * 2 + (tg & 15) * D * 2 + c * 16;
-      const int dst = mf_copy_lds<D>(wave, i, 0);  // wave-uniform base; lane l lands at +16 l
-      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)(kl + dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(vl + dst), 16, 0, 0);
+      const uint32_t off = (uint32_t)(min(tin[i] + du, lim) * ROW + coff[i]);
+      lds_char* dst = stage + (wave * NI + i) * 1024;  // lane l lands at +16 l
+      copy_to_lds(ks, off, dst);
+      copy_to_lds(vs, off, dst + S::TILE);
     }
   };
-
-  dma(0, 0);
-  for (int blk = 0; blk < nblocks; ++blk) {
-    const int stage = blk & 1;
-    if (blk + 1 < nblocks) {
-      dma(blk + 1, stage ^ 1);
-      __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI));  // block blk landed; block blk+1 may fly
-    } else {
-      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  // even blocks in stage0, odd blocks in stage1; the copy of block b+1 is
+  // issued before block b is computed.  The loop is instantiated per slice
+  // count, so a wave's state never crosses a branch inside it.
+  auto run = [&](auto ns_tag) {
+    constexpr int NSL = decltype(ns_tag)::value;
+    auto compute = [&](const lds_char* stage, int blk) {
+      if constexpr (NSL > 0) mf_block<D, NSL>(st, stage, stage + S::TILE, min(64, ntok - blk * 64), sc, ones);
+    };
+    dma(0, stage0);
+    for (int blk = 0; blk < nblocks; blk += 2) {
+      if (blk + 1 < nblocks) {
+        dma(blk + 1, stage1);
+        __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI));  // block blk landed; block blk+1 may fly
+      } else {
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      }
+      lds_barrier();  // every wave's copy of block blk has landed
+      compute(stage0, blk);
+      lds_barrier();  // stage0 consumed before block blk+2 is copied into it
+      if (blk + 1 >= nblocks) break;
+      if (blk + 2 < nblocks) {
+        dma(blk + 2, stage0);
+        __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI));
+      } else {
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      }
+      lds_barrier();
+      compute(stage1, blk + 1);
+      lds_barrier();
     }
-    __builtin_amdgcn_s_barrier();  // every wave's copy of block blk has landed
-    if (act[0]) {
-      const lds_char* Ks = (const lds_char*)(smem + stage * S::STAGE);
-      const lds_char* Vs = Ks + S::TILE;
-      // ---- S^T tiles: t = kb*2 + half covers tokens 32kb + {8*(m/4) + 4*half + m%4} ----
-      f32x4 st[2][4];
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) st[sl][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bf16x8 a[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          a[kk] = *(const __attribute__((address_space(3))) bf16x8*)(Ks + mf_k_lds<D>(t, kk, lg, l16));
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          st[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], qb[0][kk], st[0][t], 0, 0, 0);
-          if (act[1]) st[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], qb[1][kk], st[1][t], 0, 0, 0);
-        }
-      }
-      // ---- online softmax per row (lane's row = l16; 16 raw scores per lane) ----
-      if (blk * 64 + 64 > ntok) {  // last block of the chunk: mask tokens past its end
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (blk * 64 + (t >> 1) * 32 + 8 * lg + 4 * (t & 1) + i >= ntok) st[sl][t][i] = -INFINITY;
-      }
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        if (!act[sl]) continue;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[sl][t][i]);
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        mx *= sc;  // log2 units (sc > 0 keeps the order)
-        mtrue[sl] = fmaxf(mtrue[sl], mx);
-        if (__builtin_amdgcn_ballot_w64(mx > mref[sl] + kLazy)) {
-          const float mn = fmaxf(mref[sl], mx);
-          const float alpha = fast_exp2(mref[sl] - mn);
-          mref[sl] = mn;
-          lrow[sl] *= alpha;
-          rsum[sl] *= alpha;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) oacc[sl][nb] *= alpha;
-        }
-        const float nm = -mref[sl];
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          bf16x8 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = fast_exp2(fmaf(st[sl][kb * 2][i], sc, nm));  // exp2(-inf) = 0 when masked
-            const float p1 = fast_exp2(fmaf(st[sl][kb * 2 + 1][i], sc, nm));
-            ps += p0 + p1;
-            v[i] = (__bf16)p0;
-            v[4 + i] = (__bf16)p1;
-          }
-          pb[sl][kb] = v;
-          // row sum of the bf16-rounded weights used in P.V, by MFMA against ones
-          rsum[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, v, rsum[sl], 0, 0, 0);
-        }
-        lrow[sl] += ps;
-      }
-      // ---- O^T += V^T P^T; V^T operand through transposing LDS reads ----
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          v4i16 h[2];
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(Vs + mf_v_lds<D>(kb, nb, hf, lg, l16)));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][kb], oacc[0][nb], 0, 0, 0);
-          if (act[1]) oacc[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][kb], oacc[1][nb], 0, 0, 0);
-        }
-      }
-    }
-    __builtin_amdgcn_s_barrier();  // stage fully consumed before block blk+2 is copied into it
-  }
+  };
+  if (ns == 2)
+    run(std::integral_constant<int, 2>{});
+  else if (ns == 1)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 0>{});
 
   // ---- write each row's partial (or the output when the chunk is all of it) ----
   const auto ro = make_rsrc(p.part_o, p.part_o_bytes);
   const auto rm = make_rsrc(p.part_ml, p.part_ml_bytes);
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
-    if (!act[sl]) continue;
-    float L = lrow[sl];
-    L += shfl_xor(L, 16);
-    L += shfl_xor(L, 32);
-    const float Lr = rsum[sl][0];  // every element holds the row's sum
+    if (sl >= ns) continue;
+    float L = st.lrow[sl], L0, L1;
+    lane_pair<32>(L, L0, L1);
+    L = L0 + L1;
+    lane_pair<16>(L, L0, L1);
+    L = L0 + L1;
+    const float Lr = st.rsum[sl][0];  // every element holds the row's sum
     const int row = (wave + kWaves * sl) * 16 + l16;
     if (row >= rc) continue;
     const int grow = rb + row;
     const int qi = mem[grow / R], hh = grow % R;
     const float inv = 1.f / Lr;  // normalise with the sum of the rounded weights used in P.V
-    const float lt = L * fast_exp2(mref[sl] - mtrue[sl]);
+    const float lt = L * fast_exp2(st.mref[sl] - st.mtrue[sl]);
     const int E = p.expected[qi];
     const int64_t orow = (int64_t)qi * p.hq + kvh * R + hh;
     if (E == 1) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, oacc[sl][nb] * inv);
-      if (lg == 0) store_ml(p, orow, mtrue[sl], lt);
+      for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, st.o[sl][nb] * inv);
+      if (lg == 0) store_ml(p, orow, st.mtrue[sl], lt);
     } else {
       const uint32_t srow = (uint32_t)(((p.slot_off[qi] + jslot) * p.hkv + kvh) * R + hh);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) st_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u, oacc[sl][nb] * inv);
+      for (int nb = 0; nb < NB; ++nb) st_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u, st.o[sl][nb] * inv);
       if (lg == 0) {
-        st_coh1(rm, srow * 8u, mtrue[sl]);
+        st_coh1(rm, srow * 8u, st.mtrue[sl]);
         st_coh1(rm, srow * 8u + 4u, lt);
       }
     }
@@ -697,28 +810,48 @@ __device__ void empty_wave(const DecodeParams& p, const WorkItem& it) {
   }
 }
 
+// LDS: two stages of the MFMA tile (the first also holds the mat-vec tiles'
+// q rows) and the tile's arrival list; separate arrays, so the compiler can
+// tell a stage's reads from the copy into the other stage.
 template <int D, int R, bool BF16>
 struct Lds {
   static constexpr int MV = kWaves * MvShape<D, R, BF16>::QBYTES;
-  static constexpr int MF = BF16 ? MfShape<D>::LDS_BYTES : 0;
-  static constexpr int BYTES = MV > MF ? MV : MF;
+  static constexpr int MF = BF16 ? MfShape<D>::STAGE : 16;
+  static constexpr int STAGE0 = MV > MF ? MV : MF;
 };
 
 template <int D, int R, bool BF16>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[Lds<D, R, BF16>::BYTES];
+  __shared__ __attribute__((aligned(16))) char lds0[Lds<D, R, BF16>::STAGE0];
+  __shared__ __attribute__((aligned(16))) char lds1[Lds<D, R, BF16>::MF];
+  __shared__ int32_t lds_list[128 + 1];
+  const uint64_t t0 = p.trace ? __builtin_amdgcn_s_memrealtime() : 0;
   const WorkItem* unit = p.items + (int64_t)blockIdx.x * kUnitItems;
   const int kind0 = unit[0].kind & 0xff;
   if (kind0 == ITEM_PREFIX_MFMA) {
-    if constexpr (BF16) prefix_mfma_tile<D, R>(p, unit[0], smem);
-    return;
+    if constexpr (BF16)
+      prefix_mfma_tile<D, R>(p, unit[0], (lds_char*)lds0, (lds_char*)lds1, lds_list, lds_list + 128);
+  } else {
+    const WorkItem it = unit[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
+    const int kind = it.kind & 0xff;
+    if (kind == ITEM_MATVEC)
+      matvec_wave<D, R, BF16>(p, it, lds0);
+    else if (kind == ITEM_EMPTY)
+      empty_wave<D>(p, it);
   }
-  const WorkItem it = unit[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
-  const int kind = it.kind & 0xff;
-  if (kind == ITEM_MATVEC)
-    matvec_wave<D, R, BF16>(p, it, smem);
-  else if (kind == ITEM_EMPTY)
-    empty_wave<D>(p, it);
+  if (p.trace) {  // per-unit timing: start, end of the whole workgroup, where it ran
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+      const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID
+      const uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20);  // XCC_ID
+      uint64_t* t = p.trace + (int64_t)blockIdx.x * 4;
+      t[0] = t0;
+      t[1] = t1;
+      t[2] = hw | ((uint64_t)xcc << 32);
+      t[3] = (uint64_t)kind0;
+    }
+  }
 }
 
 template <int D, int R, bool BF16>

@@ -67,6 +67,7 @@ struct DecodeParams {
   int32_t hkv;
   float scale_log2;         // sm_scale * log2(e)
   int32_t out_bf16;
+  uint64_t* trace;          // optional, [num_units][4]: start, end (100 MHz clock), HW_ID | XCC_ID << 32, kind
 };
 
 }  // namespace psa
