@@ -139,6 +139,7 @@ def trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, path):
     P.psa_decode_attention(plan, q, k, v, out, ws, trace=tr)
     torch.cuda.synchronize()
     t = tr.view(units, 4).cpu().numpy()
+    np.save(path + ".npy", t)  # raw records: start, end, HW_ID | XCC_ID << 32, kind
     ok = (t[:, 0] > 0) & (t[:, 1] >= t[:, 0])
     if not ok.all():
         log(f"trace: {int((~ok).sum())} of {units} units without a valid record, e.g. {t[~ok][:3].tolist()}")

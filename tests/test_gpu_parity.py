@@ -206,13 +206,15 @@ def test_deterministic_and_reusable_workspace():
 
     wl = build_single_level("det", 32, 8, 128, "bf16", [(400, 30, (0, 300))], (4, (1, 900)), seed=6)
     q, k, v = values(wl)
-    log("case determinism x20, shuffled order, poisoned slots")
+    log("case determinism x20 (same workspace: queues and counters reset themselves), poisoned slots")
     step, out, m, l = run(wl, wl.batch, q, k, v, prefix_chunk_tokens=128, distinct_chunk_tokens=128)
-    ref = out.clone()
-    for _ in range(20):  # the same workspace: counters reset themselves
+    ref, mref, lref = out.clone(), m.clone(), l.clone()
+    for _ in range(20):
+        for t in (out, m, l):
+            t.fill_(float("nan"))
         step(q, k, v, out, m, l)
-    torch.cuda.synchronize()
-    assert torch.equal(out, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(m, mref) and torch.equal(l, lref)
     _, out2, _, _ = run(wl, wl.batch, q, k, v, prefix_chunk_tokens=128, distinct_chunk_tokens=128,
                         flags=P.NO_XCD_ORDER)
     assert torch.equal(out2, ref)
