@@ -568,25 +568,38 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
           if ((t >> 1) * 32 + 8 * lg + 4 * (t & 1) + i >= valid) s[sl][t][i] = -INFINITY;
   }
   // ---- online softmax per row (lane's row = l16; 16 raw scores per lane) ----
-  bf16x8 pb[NS][2];
+  // Maxima and the (rare) lazy rescale of every slice first, so that the
+  // exponentials and the P.V products after it form one branch-free stretch
+  // in which the scheduler can overlap a slice's exponentials with the
+  // previous slice's MFMAs.
+  float mx[NS];
+  bool up = false;
 #pragma unroll
   for (int sl = 0; sl < NS; ++sl) {
-    float mx = -INFINITY;
+    float m = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[sl][t][i]);
-    mx = max_lane_groups(mx) * sc;  // log2 units (sc > 0 keeps the order)
-    st.mtrue[sl] = fmaxf(st.mtrue[sl], mx);
-    if (__builtin_amdgcn_ballot_w64(mx > st.mref[sl] + kLazy)) {
-      const float mn = fmaxf(st.mref[sl], mx);
-      const float alpha = fast_exp2(st.mref[sl] - mn);
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, s[sl][t][i]);
+    mx[sl] = max_lane_groups(m) * sc;  // log2 units (sc > 0 keeps the order)
+    st.mtrue[sl] = fmaxf(st.mtrue[sl], mx[sl]);
+    up |= mx[sl] > st.mref[sl] + kLazy;
+  }
+  if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      const float mn = fmaxf(st.mref[sl], mx[sl]);
+      const float alpha = fast_exp2(st.mref[sl] - mn);  // 1 for a slice that did not move
       st.mref[sl] = mn;
       st.lrow[sl] *= alpha;
       st.rsum[sl] *= alpha;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) st.o[sl][nb] *= alpha;
     }
+  }
+  // ---- P (bf16) and O^T += V^T P^T, slice by slice; V^T through transposing LDS reads ----
+  bf16x8 pb[NS][2];
+  auto weights = [&](int sl) {
     const float nm = -st.mref[sl];
     float ps = 0.f;
 #pragma unroll
@@ -605,21 +618,27 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
       st.rsum[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, v, st.rsum[sl], 0, 0, 0);
     }
     st.lrow[sl] += ps;
-  }
-  // ---- O^T += V^T P^T; V^T operand through transposing LDS reads ----
+  };
+  auto pv = [&](int sl) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      v4i16 h[2];
+      for (int kb = 0; kb < 2; ++kb) {
+        v4i16 h[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(Vs + mf_v_lds<D>(kb, nb, hf, lg, l16)));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int sl = 0; sl < NS; ++sl) st.o[sl][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[sl][kb], st.o[sl][nb], 0, 0, 0);
+        for (int hf = 0; hf < 2; ++hf)
+          h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(Vs + mf_v_lds<D>(kb, nb, hf, lg, l16)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        st.o[sl][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[sl][kb], st.o[sl][nb], 0, 0, 0);
+      }
     }
+  };
+  weights(0);
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    if (sl + 1 < NS) weights(sl + 1);  // independent of pv(sl): free to interleave with it
+    pv(sl);
   }
 }
 
