@@ -109,7 +109,7 @@ typedef struct {
 typedef struct {
   uint32_t flags;
   int32_t prefix_chunk_tokens;   /* KV-range chunk of prefix work (split-K); default 2048 */
-  int32_t distinct_chunk_tokens; /* chunk of distinct work; default 512 */
+  int32_t distinct_chunk_tokens; /* chunk of distinct work, <= 1024; default 1024 */
   int32_t mfma_min_rows;         /* group rows (members * Hq/Hkv) at or above which the
                                     prefix uses the MFMA tile; default 16 */
   int32_t mfma_tile_rows;        /* max rows per MFMA prefix tile, multiple of 16, <= 128;

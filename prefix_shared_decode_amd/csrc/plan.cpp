@@ -74,7 +74,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   if ((o.flags & PSA_PLAN_PREFIX_ONLY) && (o.flags & PSA_PLAN_DISTINCT_ONLY))
     return set_error(PSA_ERR_INVALID_ARGUMENT, "PREFIX_ONLY and DISTINCT_ONLY are exclusive");
   if (o.prefix_chunk_tokens == 0) o.prefix_chunk_tokens = 2048;
-  if (o.distinct_chunk_tokens == 0) o.distinct_chunk_tokens = 512;
+  if (o.distinct_chunk_tokens == 0) o.distinct_chunk_tokens = 1024;
   if (o.mfma_min_rows == 0) o.mfma_min_rows = 16;
   if (o.mfma_tile_rows == 0) o.mfma_tile_rows = 128;
   if (o.prefix_chunk_tokens < 0 || o.prefix_chunk_tokens % c.page_size || o.distinct_chunk_tokens < 0 ||
