@@ -597,49 +597,68 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
       for (int nb = 0; nb < NB; ++nb) st.o[sl][nb] *= alpha;
     }
   }
-  // ---- P (bf16) and O^T += V^T P^T, slice by slice; V^T through transposing LDS reads ----
+  // ---- P (bf16) and O^T += V^T P^T by 32-token k-slice kb; V^T through
+  // transposing LDS reads.  The k-slice-1 weights are computed in pieces
+  // between the k-slice-0 MFMAs (the scheduler is fenced per step), so the
+  // exponentials overlap the matrix core; V^T operands are read one step
+  // ahead. ----
   bf16x8 pb[NS][2];
-  auto weights = [&](int sl) {
+  float ps[NS];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) ps[sl] = 0.f;
+  // two weights of slice sl, k-slice kb: token tile t = 2 kb + (piece >> 1),
+  // accumulator elements 2 (piece & 1) and 2 (piece & 1) + 1
+  auto wpiece = [&](int sl, int kb, int piece) {
+    const int t = kb * 2 + (piece >> 1), i0 = 2 * (piece & 1);
     const float nm = -st.mref[sl];
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = fast_exp2(fmaf(s[sl][kb * 2][i], sc, nm));  // exp2(-inf) = 0 when masked
-        const float p1 = fast_exp2(fmaf(s[sl][kb * 2 + 1][i], sc, nm));
-        ps += p0 + p1;
-        v[i] = (__bf16)p0;
-        v[4 + i] = (__bf16)p1;
-      }
-      pb[sl][kb] = v;
-      // row sum of the bf16-rounded weights used in P.V, by MFMA against ones
-      st.rsum[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, v, st.rsum[sl], 0, 0, 0);
-    }
-    st.lrow[sl] += ps;
+    const float p0 = fast_exp2(fmaf(s[sl][t][i0], sc, nm));  // exp2(-inf) = 0 when masked
+    const float p1 = fast_exp2(fmaf(s[sl][t][i0 + 1], sc, nm));
+    ps[sl] += p0 + p1;
+    const int e = (piece >> 1) * 4 + i0;
+    pb[sl][kb][e] = (__bf16)p0;
+    pb[sl][kb][e + 1] = (__bf16)p1;
   };
-  auto pv = [&](int sl) {
+  // row sum of the bf16-rounded weights used in P.V, by MFMA against ones
+  auto rowsum = [&](int kb) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        v4i16 h[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16*)(Vs + mf_v_lds<D>(kb, nb, hf, lg, l16)));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        st.o[sl][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[sl][kb], st.o[sl][nb], 0, 0, 0);
-      }
-    }
+    for (int sl = 0; sl < NS; ++sl)
+      st.rsum[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[sl][kb], st.rsum[sl], 0, 0, 0);
   };
-  weights(0);
+  auto vread = [&](int kb, int nb) {
+    v4i16 h[2];
 #pragma unroll
-  for (int sl = 0; sl < NS; ++sl) {
-    if (sl + 1 < NS) weights(sl + 1);  // independent of pv(sl): free to interleave with it
-    pv(sl);
+    for (int hf = 0; hf < 2; ++hf)
+      h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(Vs + mf_v_lds<D>(kb, nb, hf, lg, l16)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+    for (int piece = 0; piece < 4; ++piece) wpiece(sl, 0, piece);
+  rowsum(0);
+  bf16x8 vn = vread(0, 0);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const bf16x8 va = vn;
+    vn = nb + 1 < NB ? vread(0, nb + 1) : vread(1, 0);
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) st.o[sl][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[sl][0], st.o[sl][nb], 0, 0, 0);
+    if (nb < NS * 4) wpiece(nb / 4, 1, nb % 4);
+    __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int q = NB; q < NS * 4; ++q) wpiece(q / 4, 1, q % 4);  // (D 64: fewer steps than pieces)
+  rowsum(1);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const bf16x8 va = vn;
+    if (nb + 1 < NB) vn = vread(1, nb + 1);
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) st.o[sl][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[sl][1], st.o[sl][nb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) st.lrow[sl] += ps[sl];
 }
 
 template <int D, int R>
@@ -734,27 +753,23 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     auto compute = [&](const lds_char* stage, int blk) {
       if constexpr (NSL > 0) mf_block<D, NSL>(st, stage, stage + S::TILE, min(64, ntok - blk * 64), sc, ones);
     };
+    // one barrier per block: after it every wave's copy of block b has landed
+    // and every wave is done with block b - 1, whose stage then receives the
+    // copy of block b + 1 (in flight while block b is computed)
+    // one barrier per block: after it every wave's copy of block b has landed
+    // and every wave is done with block b - 1, whose stage then receives the
+    // copy of block b + 1 (in flight while block b is computed)
     dma(0, stage0);
     for (int blk = 0; blk < nblocks; blk += 2) {
-      if (blk + 1 < nblocks) {
-        dma(blk + 1, stage1);
-        __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI));  // block blk landed; block blk+1 may fly
-      } else {
-        __builtin_amdgcn_s_waitcnt(wait_vm(0));
-      }
-      lds_barrier();  // every wave's copy of block blk has landed
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));  // this wave's copy of block blk
+      lds_barrier();
+      if (blk + 1 < nblocks) dma(blk + 1, stage1);
       compute(stage0, blk);
-      lds_barrier();  // stage0 consumed before block blk+2 is copied into it
       if (blk + 1 >= nblocks) break;
-      if (blk + 2 < nblocks) {
-        dma(blk + 2, stage0);
-        __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI));
-      } else {
-        __builtin_amdgcn_s_waitcnt(wait_vm(0));
-      }
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
       lds_barrier();
+      if (blk + 2 < nblocks) dma(blk + 2, stage0);
       compute(stage1, blk + 1);
-      lds_barrier();
     }
   };
   if (ns == 2)
