@@ -106,6 +106,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 constexpr int kSc1 = 16;  // cache policy: coherent at device (agent) scope
+constexpr int kNt = 2;    // cache policy: non-temporal (streamed once; keeps reused prefix K/V and
+                          // partials from being evicted by the distinct KV stream)
 
 __device__ __forceinline__ void st_coh4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
@@ -187,7 +189,8 @@ __device__ void merge_wave(const DecodeParams& p, int qi, int kvh) {
 // over the LPT lanes with DPP; P.V uses bf16 dot2 over pairs of the lane's
 // tokens.  LPT is 8 unless R * dims-per-lane would exceed 64 accumulators.
 // The next page is in flight while one is computed; buffer loads use a descriptor covering one
-// (page, kv head) tile, so a page past the chunk reads zeros with no traffic.
+// (page, kv head) tile, so a page past the chunk reads zeros with no traffic.  Pages are
+// loaded non-temporal: each byte is read once.
 // q is staged once through LDS (per wave) and re-read per page.
 template <int D, int R, bool BF16>
 struct MvShape {
@@ -250,8 +253,8 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
 #pragma unroll
       for (int k = 0; k < NCH; ++k) {
         const uint32_t off = (uint32_t)(((ts + TSTEP * t) * D + (k * LPT + c) * EPC) * S::EB);
-        b.k[t][k] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-        b.v[t][k] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        b.k[t][k] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kNt);
+        b.v[t][k] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kNt);
       }
   };
 
