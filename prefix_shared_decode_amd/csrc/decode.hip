@@ -105,6 +105,10 @@ __device__ __forceinline__ float max_lane_groups(float v) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+#ifndef PSA_MV_PAGES
+#define PSA_MV_PAGES 2
+#endif
+constexpr int kMvPages = PSA_MV_PAGES;  // mat-vec tile: pages of K and V in flight per wave
 constexpr int kSc1 = 16;  // cache policy: coherent at device (agent) scope
 constexpr int kNt = 2;    // cache policy: non-temporal (streamed once; keeps reused prefix K/V and
                           // partials from being evicted by the distinct KV stream)
@@ -343,12 +347,14 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
       for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
     }
     bool over = false;
-    PageRegs<D, R, BF16> b0, b1;
-    load(b0, 0);
-    load(b1, 1);
+    // a ring of kMvPages page buffers: page j lives in buffer j % kMvPages,
+    // and its load is issued kMvPages pages ahead of its use
+    PageRegs<D, R, BF16> b[kMvPages];
+#pragma unroll
+    for (int u = 0; u < kMvPages; ++u) load(b[u], u);
     {
       float s[NT][R];
-      scores(b0, 0, s);
+      scores(b[0], 0, s);
       if (!fixed_ref) {
 #pragma unroll
         for (int h = 0; h < R; ++h) {
@@ -361,18 +367,20 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
           mtrue[h] = -INFINITY;
         }
       }
-      accumulate(b0, s, over);
+      accumulate(b[0], s, over);
     }
-    load(b0, 2);
-    for (int j = 1; j < npages; j += 2) {  // a page past the end is all masked zeros
-      float s1[NT][R];
-      scores(b1, j, s1);
-      accumulate(b1, s1, over);
-      load(b1, j + 2);
-      float s2[NT][R];
-      scores(b0, j + 1, s2);
-      accumulate(b0, s2, over);
-      load(b0, j + 3);
+    load(b[0], kMvPages);
+    for (int j = 1; j < npages; j += kMvPages) {
+#pragma unroll
+      for (int u = 0; u < kMvPages; ++u) {
+        const int bi = (u + 1) % kMvPages;
+        if (j + u < npages) {  // wave-uniform; loads past the end read zeros without traffic
+          float s1[NT][R];
+          scores(b[bi], j + u, s1);
+          accumulate(b[bi], s1, over);
+        }
+        load(b[bi], j + u + kMvPages);
+      }
     }
     if (!__builtin_amdgcn_ballot_w64(over)) break;
     // rare: redo with the exact per-head maximum of this chunk
@@ -530,37 +538,51 @@ struct MfRows {
   bf16x8 qb[2][D / 32];        // Q^T B operands
   f32x4 o[2][D / 16];          // O^T accumulators (unnormalised, relative to mref)
   f32x4 rsum[2];               // row sums of the bf16-rounded weights (every element)
-  float mref[2], mtrue[2];     // reference max (lazy) and true max, log2 units
+  float mref[2];               // reference max of the row (lazy), log2 units
+  float mtrue[2];              // max of the row's scores this lane has seen, log2 units
   float lrow[2];               // this lane's part of the row sum of exact weights
+  int koff[D / 32];            // this lane's LDS offsets of the tile-0 K operand reads
+  int voff[D / 16];            // and of the (kb 0, hf 0) V^T operand reads
 };
 
 // One 64-token block (K at Ks, V at Vs) for the wave's NS slices; tokens at or
 // past `valid` are masked.
-template <int D, int NS>
+template <int D, int NS, typename Copy>
 __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, const lds_char* Vs, int valid, float sc,
-                                         const bf16x8& ones) {
+                                         const bf16x8& ones, Copy&& copy) {
   constexpr int KK = D / 32, NB = D / 16;
-  // an opaque lane index: the LDS offsets derived from it are recomputed per
-  // block instead of being held in registers across the loop
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));
-  const int l16 = lane & 15, lg = lane >> 4;
+  const int lg = (threadIdx.x & 63) >> 4;
   // ---- S^T tiles: t = kb*2 + half covers tokens 32kb + {8*(m/4) + 4*half + m%4} ----
   f32x4 s[NS][4];
 #pragma unroll
   for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
     for (int t = 0; t < 4; ++t) s[sl][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // K operands of token tiles t and t + 1 are in flight while tile t - 1's
+  // MFMAs issue; one piece of the next block's copy follows each tile's
+  // MFMAs, so that a stall on issuing it (the load path is shared with the
+  // other workgroup on the CU) leaves queued matrix work behind it.
+  bf16x8 a[2][KK];
+  auto kread = [&](int t) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      a[t & 1][kk] = *(const __attribute__((address_space(3))) bf16x8*)(Ks + st.koff[kk] + mf_k_step<D>(t));
+  };
+  kread(0);
+  kread(1);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    bf16x8 a[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) a[kk] = *(const __attribute__((address_space(3))) bf16x8*)(Ks + mf_k_lds<D>(t, kk, lg, l16));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int sl = 0; sl < NS; ++sl) s[sl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], st.qb[sl][kk], s[sl][t], 0, 0, 0);
+      for (int sl = 0; sl < NS; ++sl)
+        s[sl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t & 1][kk], st.qb[sl][kk], s[sl][t], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 2 < 4) kread(t + 2);
+    copy(t);
   }
+  __builtin_amdgcn_sched_barrier(0);
   if (valid < 64) {  // last block of the chunk: mask tokens past its end
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl)
@@ -571,10 +593,11 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
           if ((t >> 1) * 32 + 8 * lg + 4 * (t & 1) + i >= valid) s[sl][t][i] = -INFINITY;
   }
   // ---- online softmax per row (lane's row = l16; 16 raw scores per lane) ----
-  // Maxima and the (rare) lazy rescale of every slice first, so that the
-  // exponentials and the P.V products after it form one branch-free stretch
-  // in which the scheduler can overlap a slice's exponentials with the
-  // previous slice's MFMAs.
+  // Each lane checks its own scores against the row's reference max; only
+  // when one exceeds it by kLazy (rare) does the wave take the row maxima
+  // across lane groups and rescale.  Maxima and the rescale come first, so
+  // that the exponentials and the P.V products after them form one
+  // branch-free stretch.
   float mx[NS];
   bool up = false;
 #pragma unroll
@@ -584,14 +607,14 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) m = fmaxf(m, s[sl][t][i]);
-    mx[sl] = max_lane_groups(m) * sc;  // log2 units (sc > 0 keeps the order)
+    mx[sl] = m * sc;  // log2 units (sc > 0 keeps the order)
     st.mtrue[sl] = fmaxf(st.mtrue[sl], mx[sl]);
     up |= mx[sl] > st.mref[sl] + kLazy;
   }
   if (__builtin_amdgcn_ballot_w64(up)) {
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
-      const float mn = fmaxf(st.mref[sl], mx[sl]);
+      const float mn = fmaxf(st.mref[sl], max_lane_groups(mx[sl]));
       const float alpha = fast_exp2(st.mref[sl] - mn);  // 1 for a slice that did not move
       st.mref[sl] = mn;
       st.lrow[sl] *= alpha;
@@ -632,7 +655,7 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
       h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4i16*)(Vs + mf_v_lds<D>(kb, nb, hf, lg, l16)));
+          (__attribute__((address_space(3))) v4i16*)(Vs + st.voff[nb] + mf_v_step<D>(kb, hf)));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
 #pragma unroll
@@ -708,6 +731,10 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     st.mtrue[sl] = -INFINITY;
     st.lrow[sl] = 0.f;
   }
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) st.koff[kk] = mf_k_base<D>(kk, lg, l16);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) st.voff[nb] = mf_v_base<D>(nb, lg, l16);
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
@@ -720,6 +747,11 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(st.qb[sl][kk]));
   asm volatile("" ::"v"(pid_v));
+  // the LDS offsets are held in registers for the whole loop
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(st.koff[kk]));
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(st.voff[nb]));
 
   // copy of one 64-token block into a stage, global -> LDS through the load
   // unit: this wave's NI loads per tile (index maps in layout.h) all fall in
@@ -732,47 +764,66 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     coff[i] = mf_copy_chunk<D>(wave, i, lane) * 16;
   }
   const int64_t tile_stride = (int64_t)p.hkv * TILEB;
-  auto dma = [&](int blk, lds_char* stage) {
+  // where this wave's copy of block blk comes from: K and V tile bases and
+  // the token clamp (tokens past the chunk re-read its last token)
+  struct Src {
+    const char* ks;
+    const char* vs;
+    int du, lim;
+  };
+  auto src = [&](int blk) {
     const int pg = min(blk * 4 + wave, npages - 1);
     const int pid = __builtin_amdgcn_readlane(pid_v, blk);
-    const int du = (blk * 4 + wave - pg) * 16;  // > 0 only when this wave's page is past the chunk
-    const int lim = ntok - 1 - pg * 16;         // last valid token within the page
     const int64_t tile = (int64_t)pid * tile_stride + (int64_t)kvh * TILEB;
-    const char* ks = kp + tile;
-    const char* vs = vp + tile;
+    // du > 0 only when this wave's page is past the chunk; lim = last valid token within the page
+    return Src{kp + tile, vp + tile, (blk * 4 + wave - pg) * 16, ntok - 1 - pg * 16};
+  };
+  // load i (of NI) of K and of V into a stage; lane l lands at +16 l
+  auto dma_piece = [&](const Src& c, lds_char* stage, int i) {
+    const uint32_t off = (uint32_t)(min(tin[i] + c.du, c.lim) * ROW + coff[i]);
+    lds_char* dst = stage + (wave * NI + i) * 1024;
+    copy_to_lds(c.ks, off, dst);
+    copy_to_lds(c.vs, off, dst + S::TILE);
+  };
+  auto dma = [&](int blk, lds_char* stage) {
+    const Src c = src(blk);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const uint32_t off = (uint32_t)(min(tin[i] + du, lim) * ROW + coff[i]);
-      lds_char* dst = stage + (wave * NI + i) * 1024;  // lane l lands at +16 l
-      copy_to_lds(ks, off, dst);
-      copy_to_lds(vs, off, dst + S::TILE);
-    }
+    for (int i = 0; i < NI; ++i) dma_piece(c, stage, i);
   };
   // even blocks in stage0, odd blocks in stage1; the copy of block b+1 is
   // issued before block b is computed.  The loop is instantiated per slice
   // count, so a wave's state never crosses a branch inside it.
   auto run = [&](auto ns_tag) {
     constexpr int NSL = decltype(ns_tag)::value;
-    auto compute = [&](const lds_char* stage, int blk) {
-      if constexpr (NSL > 0) mf_block<D, NSL>(st, stage, stage + S::TILE, min(64, ntok - blk * 64), sc, ones);
+    // compute block blk from `stage` while copying block blk + 1 (if any) into `next`
+    auto compute = [&](const lds_char* stage, int blk, lds_char* next) {
+      const bool more = blk + 1 < nblocks;
+      const Src c = src(more ? blk + 1 : blk);
+      auto copy = [&](int t) {  // NI pieces spread over the 4 token tiles
+        if (more) {
+#pragma unroll
+          for (int i = t * NI / 4; i < (t + 1) * NI / 4; ++i) dma_piece(c, next, i);
+        }
+      };
+      if constexpr (NSL > 0) {
+        mf_block<D, NSL>(st, stage, stage + S::TILE, min(64, ntok - blk * 64), sc, ones, copy);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) copy(t);
+      }
     };
     // one barrier per block: after it every wave's copy of block b has landed
     // and every wave is done with block b - 1, whose stage then receives the
-    // copy of block b + 1 (in flight while block b is computed)
-    // one barrier per block: after it every wave's copy of block b has landed
-    // and every wave is done with block b - 1, whose stage then receives the
-    // copy of block b + 1 (in flight while block b is computed)
+    // copy of block b + 1 (issued in pieces while block b is computed)
     dma(0, stage0);
     for (int blk = 0; blk < nblocks; blk += 2) {
       __builtin_amdgcn_s_waitcnt(wait_vm(0));  // this wave's copy of block blk
       lds_barrier();
-      if (blk + 1 < nblocks) dma(blk + 1, stage1);
-      compute(stage0, blk);
+      compute(stage0, blk, stage1);
       if (blk + 1 >= nblocks) break;
       __builtin_amdgcn_s_waitcnt(wait_vm(0));
       lds_barrier();
-      if (blk + 2 < nblocks) dma(blk + 2, stage0);
-      compute(stage1, blk + 1);
+      compute(stage1, blk + 1, stage0);
     }
   };
   if (ns == 2)
@@ -794,6 +845,7 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     lane_pair<16>(L, L0, L1);
     L = L0 + L1;
     const float Lr = st.rsum[sl][0];  // every element holds the row's sum
+    st.mtrue[sl] = max_lane_groups(st.mtrue[sl]);
     const int row = (wave + kWaves * sl) * 16 + l16;
     if (row >= rc) continue;
     const int grow = rb + row;

@@ -35,13 +35,17 @@ struct MfLayout {
   static_assert(NI * WAVES * 1024 == TILE, "tile must split into whole KiB loads per wave");
 };
 
-// chunk XOR key of token t (t within a 64-token block): a bijection of the 16
-// tokens of a K operand tile onto distinct chunks, and distinct chunk pairs
-// for the 4 rows x 2 lane groups a transposing V read touches per pass
+// chunk XOR key of token t (t within a 64-token block).  Any key that is a
+// function of the token keeps the copy and the reads consistent; this one
+// (token bits 0, 1, 3, 4 for D 128; 0, 1, 3 for D 64) was chosen by timing
+// every key made of token bits on gfx950: with it the K operand reads
+// (ds_read_b128) and the transposing V reads run at the rate of
+// conflict-free linear reads, while e.g. the same bits in the order
+// 4, 3, 0, 1 make the K reads 1.55x slower.
 template <int D>
 PSA_HD int kswz(int t) {
-  if (D == 128) return ((t >> 4) & 1) | (((t >> 3) & 1) << 1) | ((t & 3) << 2);
-  return ((t >> 4) & 1) | (((t >> 3) & 1) << 1) | (((t >> 1) & 1) << 2);
+  if (D == 128) return (t & 3) | (((t >> 3) & 3) << 2);
+  return (t & 3) | (((t >> 3) & 1) << 2);
 }
 
 // copy: token and logical chunk fetched by (wave, load i, lane); LDS byte offset written
@@ -69,6 +73,16 @@ PSA_HD int mf_k_lds(int t, int kk, int lg, int l16) {
   return tok * MfLayout<D>::ROW + (((kk * 4 + lg) ^ kswz<D>(tok)) << 4);
 }
 
+// The key of a K operand token depends only on the lane (token bits 0, 1, 3,
+// 4 come from l16), so the read of tile t is the tile-0 read plus a step
+// that depends on t alone; likewise the V^T read of (kb, hf) is the (0, 0)
+// read plus a step.  The kernel holds the per-lane bases in registers and
+// adds the steps as immediates.
+template <int D>
+PSA_HD int mf_k_base(int kk, int lg, int l16) { return mf_k_lds<D>(0, kk, lg, l16); }
+template <int D>
+PSA_HD constexpr int mf_k_step(int t) { return ((t >> 1) * 32 + 4 * (t & 1)) * MfLayout<D>::ROW; }
+
 // V^T operand read (ds_read_b64_tr_b16): 8 bytes
 template <int D>
 PSA_HD int mf_v_token(int kb, int hf, int lg, int l16) {
@@ -80,5 +94,10 @@ PSA_HD int mf_v_lds(int kb, int nb, int hf, int lg, int l16) {
   const int cb = nb * 32 + (l16 & 3) * 8;
   return tok * MfLayout<D>::ROW + ((((cb >> 4) ^ kswz<D>(tok)) << 4) | (cb & 15));
 }
+
+template <int D>
+PSA_HD int mf_v_base(int nb, int lg, int l16) { return mf_v_lds<D>(0, nb, 0, lg, l16); }
+template <int D>
+PSA_HD constexpr int mf_v_step(int kb, int hf) { return (kb * 32 + 4 * hf) * MfLayout<D>::ROW; }
 
 }  // namespace psa

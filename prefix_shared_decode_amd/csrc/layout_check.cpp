@@ -1,11 +1,11 @@
 // Host check of the MFMA prefix tile's LDS index maps (layout.h): every lane,
 // wave and load of the copy stays inside the tile and writes each (token,
 // chunk) exactly once; every operand read stays inside the tile and finds the
-// (token, chunk) the MFMA layout expects; the K operand reads of a tile and
-// the transposing V reads hit distinct LDS bank groups.  Exit status 0 = ok.
+// (token, chunk) the MFMA layout expects.  (Bank conflicts are not modelled
+// here: the XOR key was chosen by timing the reads on the hardware.)  Exit
+// status 0 = ok.
 #include <cstdio>
 #include <cstdlib>
-#include <set>
 #include <vector>
 
 #include "layout.h"
@@ -45,35 +45,27 @@ void check() {
   // K operand reads: 16 tokens of a tile, one logical chunk per lane group
   for (int t = 0; t < 4; ++t)
     for (int kk = 0; kk < D / 32; ++kk)
-      for (int lg = 0; lg < 4; ++lg) {
-        std::set<int> banks;
+      for (int lg = 0; lg < 4; ++lg)
         for (int l16 = 0; l16 < 16; ++l16) {
           const int tok = mf_k_token<D>(t, l16);
           const int off = mf_k_lds<D>(t, kk, lg, l16);
           CHECK(off >= 0 && off + 16 <= L::TILE, "D=%d K read out of the tile", D);
           CHECK(off == at[tok * L::CPT + kk * 4 + lg], "D=%d K read misses its chunk", D);
-          banks.insert((off >> 4) & 15);  // 64 banks x 4 bytes = 16 groups of 16 bytes
+          CHECK(off == mf_k_base<D>(kk, lg, l16) + mf_k_step<D>(t), "D=%d K read is not base + step", D);
         }
-        CHECK((int)banks.size() == 16, "D=%d K operand reads conflict (%zu bank groups)", D, banks.size());
-      }
   // V^T reads: each lane's 8 bytes are 4 dims of one token; pass = 32 lanes
   for (int kb = 0; kb < 2; ++kb)
     for (int nb = 0; nb < D / 16; ++nb)
       for (int hf = 0; hf < 2; ++hf)
-        for (int pass = 0; pass < 2; ++pass) {
-          std::set<int> words;
-          for (int lane = pass * 32; lane < pass * 32 + 32; ++lane) {
-            const int lg = lane >> 4, l16 = lane & 15;
-            const int tok = mf_v_token<D>(kb, hf, lg, l16);
-            const int off = mf_v_lds<D>(kb, nb, hf, lg, l16);
-            const int cb = nb * 32 + (l16 & 3) * 8;
-            CHECK(tok >= 0 && tok < 64, "D=%d V token out of the block", D);
-            CHECK(off >= 0 && off + 8 <= L::TILE && off % 8 == 0, "D=%d V read out of the tile", D);
-            CHECK(off - (cb & 15) == at[tok * L::CPT + (cb >> 4)], "D=%d V read misses its chunk", D);
-            words.insert((off >> 2) & 63);
-            words.insert(((off >> 2) + 1) & 63);
-          }
-          CHECK((int)words.size() == 64, "D=%d V reads conflict (%zu banks)", D, words.size());
+        for (int lane = 0; lane < 64; ++lane) {
+          const int lg = lane >> 4, l16 = lane & 15;
+          const int tok = mf_v_token<D>(kb, hf, lg, l16);
+          const int off = mf_v_lds<D>(kb, nb, hf, lg, l16);
+          const int cb = nb * 32 + (l16 & 3) * 8;
+          CHECK(tok >= 0 && tok < 64, "D=%d V token out of the block", D);
+          CHECK(off >= 0 && off + 8 <= L::TILE && off % 8 == 0, "D=%d V read out of the tile", D);
+          CHECK(off - (cb & 15) == at[tok * L::CPT + (cb >> 4)], "D=%d V read misses its chunk", D);
+          CHECK(off == mf_v_base<D>(nb, lg, l16) + mf_v_step<D>(kb, hf), "D=%d V read is not base + step", D);
         }
 }
 
