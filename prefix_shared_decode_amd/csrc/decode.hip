@@ -154,33 +154,60 @@ __device__ __forceinline__ void store_ml(const DecodeParams& p, int64_t row, flo
 }
 
 // Merge the E partials of (query qi, kv head kvh) in slot order and write the
-// output; one wave.  Partials hold O normalised, m (log2 units), l.
+// output; one wave.  Partials hold O normalised, m (log2 units), l.  No
+// multiply-add is contracted here, so that the MFMA tile's merge in registers
+// (same operations, same order) gives the same bits.
 template <int D, int R>
 __device__ void merge_wave(const DecodeParams& p, int qi, int kvh) {
+#pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int E = p.expected[qi];
   const int64_t s0 = p.slot_off[qi];
   const auto ro = make_rsrc(p.part_o, p.part_o_bytes);
   const auto rm = make_rsrc(p.part_ml, p.part_ml_bytes);
-  constexpr int C4 = D / 4;  // float4 chunks per row
-  for (int ci = lane; ci < R * C4; ci += 64) {
-    const int hh = ci / C4, c4 = ci % C4;
-    float M = kNoMax;
-    for (int j = 0; j < E; ++j) {
-      const uint32_t slot = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
-      M = fmaxf(M, ld_coh1(rm, slot * 8u));
+  constexpr int C4 = D / 4;                  // float4 chunks per row
+  constexpr int NCI = (R * C4 + 63) / 64;    // chunks per lane; their loads are in flight together
+  int hh[NCI], c4[NCI];
+  bool ok[NCI];
+#pragma unroll
+  for (int k = 0; k < NCI; ++k) {
+    const int ci = lane + 64 * k;
+    ok[k] = ci < R * C4;
+    hh[k] = ok[k] ? ci / C4 : 0;
+    c4[k] = ci % C4;
+  }
+  float M[NCI];
+#pragma unroll
+  for (int k = 0; k < NCI; ++k) M[k] = kNoMax;
+#pragma unroll 2
+  for (int j = 0; j < E; ++j)
+#pragma unroll
+    for (int k = 0; k < NCI; ++k) {
+      const uint32_t slot = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh[k]);
+      M[k] = fmaxf(M[k], ld_coh1(rm, slot * 8u));
     }
-    float L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < E; ++j) {
-      const uint32_t slot = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
-      const float w = ld_coh1(rm, slot * 8u + 4u) * fast_exp2(ld_coh1(rm, slot * 8u) - M);
-      L += w;
-      acc += w * ld_coh4(ro, (slot * D + c4 * 4) * 4u);
+  float L[NCI];
+  f32x4 acc[NCI];
+#pragma unroll
+  for (int k = 0; k < NCI; ++k) {
+    L[k] = 0.f;
+    acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll 2
+  for (int j = 0; j < E; ++j)
+#pragma unroll
+    for (int k = 0; k < NCI; ++k) {
+      const uint32_t slot = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh[k]);
+      const float w = ld_coh1(rm, slot * 8u + 4u) * fast_exp2(ld_coh1(rm, slot * 8u) - M[k]);
+      L[k] += w;
+      acc[k] += w * ld_coh4(ro, (slot * D + c4[k] * 4) * 4u);
     }
-    const int64_t row = (int64_t)qi * p.hq + kvh * R + hh;
-    store_out4(p, row * D + c4 * 4, acc * (1.f / L));
-    if (c4 == 0) store_ml(p, row, M, L);
+#pragma unroll
+  for (int k = 0; k < NCI; ++k) {
+    if (!ok[k]) continue;
+    const int64_t row = (int64_t)qi * p.hq + kvh * R + hh[k];
+    store_out4(p, row * D + c4[k] * 4, acc[k] * (1.f / L[k]));
+    if (c4[k] == 0) store_ml(p, row, M[k], L[k]);
   }
 }
 
@@ -688,8 +715,7 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
 }
 
 template <int D, int R>
-__device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_char* stage0, lds_char* stage1,
-                                 int32_t* s_list, int* s_n) {
+__device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_char* stage0, lds_char* stage1) {
   using S = MfShape<D>;
   constexpr int KK = S::KK, NB = S::NB, NI = S::NI;
   constexpr int ROW = MfLayout<D>::ROW, TILEB = 16 * D * 2;  // bytes of one (page, kv head) tile
@@ -847,42 +873,85 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     const float Lr = st.rsum[sl][0];  // every element holds the row's sum
     st.mtrue[sl] = max_lane_groups(st.mtrue[sl]);
     const int row = (wave + kWaves * sl) * 16 + l16;
-    if (row >= rc) continue;
-    const int grow = rb + row;
+    const bool valid = row < rc;
+    const int grow = rb + min(row, rc - 1);  // a query's R rows lie in one slice (R divides 16)
     const int qi = mem[grow / R], hh = grow % R;
     const float inv = 1.f / Lr;  // normalise with the sum of the rounded weights used in P.V
-    const float lt = L * fast_exp2(st.mref[sl] - st.mtrue[sl]);
+    const float mt = st.mtrue[sl];
+    const float lt = L * fast_exp2(st.mref[sl] - mt);
     const int E = p.expected[qi];
     const int64_t orow = (int64_t)qi * p.hq + kvh * R + hh;
-    if (E == 1) {
+    int32_t* ctr = p.counters + (int64_t)qi * p.hkv + kvh;
+    // One lane per (query, kv head) looks at its arrival counter: when all the
+    // other pieces have arrived, this tile is the last one and merges in
+    // registers (dec 1); otherwise it writes a partial and arrives (dec 2).
+    const bool head = valid && lg == 0 && hh == 0;
+    int dec = 0;
+    if (head && E > 1) dec = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == E - 1 ? 1 : 2;
+    dec = __shfl(dec, l16 - hh);  // the query's head-0 row, lane group 0
+    if (valid) {
+      if (E == 1) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, st.o[sl][nb] * inv);
-      if (lg == 0) store_ml(p, orow, st.mtrue[sl], lt);
-    } else {
-      const uint32_t srow = (uint32_t)(((p.slot_off[qi] + jslot) * p.hkv + kvh) * R + hh);
+        for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, st.o[sl][nb] * inv);
+        if (lg == 0) store_ml(p, orow, mt, lt);
+      } else if (dec == 1) {
+        // the merge of the E partials in slot order, with the operations of
+        // merge_wave (uncontracted), this tile's own partial (slot jslot)
+        // taken from registers
+#pragma clang fp contract(off)
+        const int64_t s0 = p.slot_off[qi];
+        float M = kNoMax;
+        for (int j = 0; j < E; ++j) {
+          const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
+          M = fmaxf(M, j == jslot ? mt : ld_coh1(rm, srow * 8u));
+        }
+        float Ls = 0.f;
+        f32x4 acc[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) st_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u, st.o[sl][nb] * inv);
-      if (lg == 0) {
-        st_coh1(rm, srow * 8u, st.mtrue[sl]);
-        st_coh1(rm, srow * 8u + 4u, lt);
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < E; ++j) {
+          const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
+          if (j == jslot) {
+            const float w = lt * fast_exp2(mt - M);
+            Ls += w;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] += w * (st.o[sl][nb] * inv);
+          } else {
+            const float w = ld_coh1(rm, srow * 8u + 4u) * fast_exp2(ld_coh1(rm, srow * 8u) - M);
+            Ls += w;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] += w * ld_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u);
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, acc[nb] * (1.f / Ls));
+        if (lg == 0) store_ml(p, orow, M, Ls);
+      } else {
+        const uint32_t srow = (uint32_t)(((p.slot_off[qi] + jslot) * p.hkv + kvh) * R + hh);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) st_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u, st.o[sl][nb] * inv);
+        if (lg == 0) {
+          st_coh1(rm, srow * 8u, mt);
+          st_coh1(rm, srow * 8u + 4u, lt);
+        }
       }
     }
-  }
-  // ---- arrivals of the tile's member queries; last arrivers merge ----
-  release_partials();
-  if (tid == 0) *s_n = 0;
-  __syncthreads();
-  const int nq = rc / R;
-  for (int t = tid; t < nq; t += kThreads) {
-    const int qi = mem[rb / R + t];
-    const int E = p.expected[qi];
-    if (E >= 2 && arrive_counter(p.counters + (int64_t)qi * p.hkv + kvh) == E - 1) s_list[atomicAdd(s_n, 1)] = qi;
-  }
-  __syncthreads();
-  const int nl = *s_n;
-  for (int t = wave; t < nl; t += kWaves) {
-    merge_wave<D, R>(p, s_list[t], kvh);
-    if (lane == 0) reset_counter(p.counters + (int64_t)s_list[t] * p.hkv + kvh);
+    if (head && dec == 1) reset_counter(ctr);  // no other piece touches it in this launch
+    // arrivals of the partials written above (one wave holds all rows of a
+    // query); the last arrivers merge
+    if (__builtin_amdgcn_ballot_w64(dec == 2)) {
+      release_partials();
+      bool last = false;
+      if (head && dec == 2) last = arrive_counter(ctr) == E - 1;
+      uint64_t lm = __builtin_amdgcn_ballot_w64(last);
+      while (lm) {
+        const int src = __builtin_ctzll(lm);
+        lm &= lm - 1;
+        const int q = __builtin_amdgcn_readlane(qi, src);
+        merge_wave<D, R>(p, q, kvh);
+        if (lane == 0) reset_counter(p.counters + (int64_t)q * p.hkv + kvh);
+      }
+    }
   }
 }
 
@@ -913,13 +982,12 @@ template <int D, int R, bool BF16>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lds0[Lds<D, R, BF16>::STAGE0];
   __shared__ __attribute__((aligned(16))) char lds1[Lds<D, R, BF16>::MF];
-  __shared__ int32_t lds_list[128 + 1];
   const uint64_t t0 = p.trace ? __builtin_amdgcn_s_memrealtime() : 0;
   const WorkItem* unit = p.items + (int64_t)blockIdx.x * kUnitItems;
   const int kind0 = unit[0].kind & 0xff;
   if (kind0 == ITEM_PREFIX_MFMA) {
     if constexpr (BF16)
-      prefix_mfma_tile<D, R>(p, unit[0], (lds_char*)lds0, (lds_char*)lds1, lds_list, lds_list + 128);
+      prefix_mfma_tile<D, R>(p, unit[0], (lds_char*)lds0, (lds_char*)lds1);
   } else {
     const WorkItem it = unit[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
     const int kind = it.kind & 0xff;
