@@ -16,9 +16,10 @@ extern "C" {
  * 8 int32 per item = {kind | chunk << 8, kv_head, id, tok_begin, tok_end,
  * page_base, a, b}.  kind 0 = nothing, 1 = mat-vec over query `id`'s pages
  * (page_base indexes group pages followed by query pages; a = partials of the
- * query, b = its partial slot or -1), 2 = MFMA prefix tile over rows
- * [a, a + b) of group `id` (row = member * Hq/Hkv + head in kv group; only
- * as the first item of a unit), 3 = empty partial of query `id`.
+ * query, b = its partial slot or -1), 2 = MFMA prefix tile of group `id`
+ * over rows [a, a + b), rows counted over the plan's whole member array
+ * (row = (first member of the group + member) * Hq/Hkv + head in kv group;
+ * only as the first item of a unit), 3 = empty partial of query `id`.
  * capacity_items must be >= 4 * num_items. */
 psa_status psa_plan_debug_items(const psa_plan* plan, int32_t* out, int64_t capacity_items);
 

@@ -721,63 +721,27 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
   constexpr int ROW = MfLayout<D>::ROW, TILEB = 16 * D * 2;  // bytes of one (page, kv head) tile
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
-  const int g = it.id, kvh = it.kvh, rb = it.a, rc = it.b, jslot = it.kind >> 8;
+  const int kvh = it.kvh, rb = it.a, rc = it.b, jslot = it.kind >> 8;
   const int ntok = it.tok_end - it.tok_begin, npages = (ntok + 15) >> 4, nblocks = (ntok + 63) >> 6;
-  const int32_t* mem = p.members + p.member_off[g];
   const int nslices = (rc + 15) >> 4;
   const int ns = wave + kWaves < nslices ? 2 : (wave < nslices ? 1 : 0);
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
   const char* kp = reinterpret_cast<const char*>(p.k);
   const char* vp = reinterpret_cast<const char*>(p.v);
 
-  // lane j holds the id of the page this wave copies in block j (page 4j+wave
-  // of the chunk, clamped to its last page); a chunk has at most 32 blocks
+  // The loads before the loop form two short chains that run side by side:
+  // page ids -> copy of block 0, and member queries -> Q rows.  (Rows are
+  // counted over the whole member array, so no group offset is read first.)
+  // Lane j holds the id of the page this wave copies in block j (page 4j+wave
+  // of the chunk, clamped to its last page); a chunk has at most 32 blocks.
   int pid_v = 0;
   if (lane < nblocks) pid_v = p.pages[it.page_base + min(lane * 4 + wave, npages - 1)];
-
-  MfRows<D> st;
+  int qrow[2];
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
     const int row = (wave + kWaves * sl) * 16 + l16;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (sl < ns && row < rc) {
-        const int grow = rb + row;
-        const int qi = mem[grow / R];
-        const int64_t off = ((int64_t)qi * p.hq + kvh * R + grow % R) * D + kk * 32 + lg * 8;
-        w = *reinterpret_cast<const u32x4*>(qp + off);
-      }
-      st.qb[sl][kk] = __builtin_bit_cast(bf16x8, w);
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) st.o[sl][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.rsum[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.mref[sl] = kNoMax;
-    st.mtrue[sl] = -INFINITY;
-    st.lrow[sl] = 0.f;
+    qrow[sl] = (sl < ns && row < rc) ? p.members[(rb + row) / R] : -1;
   }
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) st.koff[kk] = mf_k_base<D>(kk, lg, l16);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) st.voff[nb] = mf_v_base<D>(nb, lg, l16);
-  bf16x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
-  const float sc = p.scale_log2;
-  // Use the loaded registers once here, so that the compiler waits for their
-  // loads before the block loop rather than at a first use inside it (a wait
-  // there would also wait for the copies in flight).
-#pragma unroll
-  for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(st.qb[sl][kk]));
-  asm volatile("" ::"v"(pid_v));
-  // the LDS offsets are held in registers for the whole loop
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(st.koff[kk]));
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(st.voff[nb]));
 
   // copy of one 64-token block into a stage, global -> LDS through the load
   // unit: this wave's NI loads per tile (index maps in layout.h) all fall in
@@ -811,10 +775,68 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     copy_to_lds(c.ks, off, dst);
     copy_to_lds(c.vs, off, dst + S::TILE);
   };
-  auto dma = [&](int blk, lds_char* stage) {
-    const Src c = src(blk);
+  {
+    const Src c = src(0);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma_piece(c, stage, i);
+    for (int i = 0; i < NI; ++i) dma_piece(c, stage0, i);
+  }
+
+  MfRows<D> st;
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (qrow[sl] >= 0) {
+        const int grow = rb + (wave + kWaves * sl) * 16 + l16;
+        const int64_t off = ((int64_t)qrow[sl] * p.hq + kvh * R + grow % R) * D + kk * 32 + lg * 8;
+        w = *reinterpret_cast<const u32x4*>(qp + off);
+      }
+      st.qb[sl][kk] = __builtin_bit_cast(bf16x8, w);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) st.o[sl][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.rsum[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.mref[sl] = kNoMax;
+    st.mtrue[sl] = -INFINITY;
+    st.lrow[sl] = 0.f;
+  }
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) st.koff[kk] = mf_k_base<D>(kk, lg, l16);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) st.voff[nb] = mf_v_base<D>(nb, lg, l16);
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+  const float sc = p.scale_log2;
+  // Use the loaded registers once here, so that the compiler waits for their
+  // loads before the block loop rather than at a first use inside it (a wait
+  // there would also wait for the copies in flight).
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(st.qb[sl][kk]));
+  asm volatile("" ::"v"(pid_v));
+  // the LDS offsets are held in registers for the whole loop
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(st.koff[kk]));
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(st.voff[nb]));
+
+  // Arrival counters of the rows' (query, kv head) pairs, read by the head-0
+  // lane of each query when the last block starts: if every other piece has
+  // arrived by then, the tile merges in registers at the end.  (A piece that
+  // arrives later is merged the slow way: read or written, the decision is
+  // sound.)
+  int cval[2] = {-1, -1};
+  auto read_counters = [&]() {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int grow = rb + (wave + kWaves * sl) * 16 + l16;
+      if (qrow[sl] >= 0 && lg == 0 && grow % R == 0 && p.expected[qrow[sl]] > 1)
+        cval[sl] = __hip_atomic_load(p.counters + (int64_t)qrow[sl] * p.hkv + kvh, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    }
   };
   // even blocks in stage0, odd blocks in stage1; the copy of block b+1 is
   // issued before block b is computed.  The loop is instantiated per slice
@@ -841,14 +863,15 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     // one barrier per block: after it every wave's copy of block b has landed
     // and every wave is done with block b - 1, whose stage then receives the
     // copy of block b + 1 (issued in pieces while block b is computed)
-    dma(0, stage0);
     for (int blk = 0; blk < nblocks; blk += 2) {
       __builtin_amdgcn_s_waitcnt(wait_vm(0));  // this wave's copy of block blk
       lds_barrier();
+      if (blk + 1 == nblocks) read_counters();
       compute(stage0, blk, stage1);
       if (blk + 1 >= nblocks) break;
       __builtin_amdgcn_s_waitcnt(wait_vm(0));
       lds_barrier();
+      if (blk + 2 == nblocks) read_counters();
       compute(stage1, blk + 1, stage0);
     }
   };
@@ -874,20 +897,20 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     st.mtrue[sl] = max_lane_groups(st.mtrue[sl]);
     const int row = (wave + kWaves * sl) * 16 + l16;
     const bool valid = row < rc;
-    const int grow = rb + min(row, rc - 1);  // a query's R rows lie in one slice (R divides 16)
-    const int qi = mem[grow / R], hh = grow % R;
+    const int grow = rb + row;  // a query's R rows lie in one slice (R divides 16)
+    const int qi = valid ? qrow[sl] : 0, hh = grow % R;
     const float inv = 1.f / Lr;  // normalise with the sum of the rounded weights used in P.V
     const float mt = st.mtrue[sl];
     const float lt = L * fast_exp2(st.mref[sl] - mt);
     const int E = p.expected[qi];
     const int64_t orow = (int64_t)qi * p.hq + kvh * R + hh;
     int32_t* ctr = p.counters + (int64_t)qi * p.hkv + kvh;
-    // One lane per (query, kv head) looks at its arrival counter: when all the
-    // other pieces have arrived, this tile is the last one and merges in
+    // One lane per (query, kv head) has read its arrival counter: when all
+    // the other pieces had arrived, this tile is the last one and merges in
     // registers (dec 1); otherwise it writes a partial and arrives (dec 2).
     const bool head = valid && lg == 0 && hh == 0;
     int dec = 0;
-    if (head && E > 1) dec = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == E - 1 ? 1 : 2;
+    if (head && E > 1) dec = cval[sl] == E - 1 ? 1 : 2;
     dec = __shfl(dec, l16 - hh);  // the query's head-0 row, lane group 0
     if (valid) {
       if (E == 1) {
@@ -900,32 +923,57 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
         // taken from registers
 #pragma clang fp contract(off)
         const int64_t s0 = p.slot_off[qi];
-        float M = kNoMax;
-        for (int j = 0; j < E; ++j) {
-          const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
-          M = fmaxf(M, j == jslot ? mt : ld_coh1(rm, srow * 8u));
-        }
-        float Ls = 0.f;
-        f32x4 acc[NB];
+        if (E == 2) {  // one other piece: its m, l and O in one round trip
+          const int jo = 1 - jslot;
+          const uint32_t srow = (uint32_t)(((s0 + jo) * p.hkv + kvh) * R + hh);
+          const float mo = ld_coh1(rm, srow * 8u), lo = ld_coh1(rm, srow * 8u + 4u);
+          f32x4 oo[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < E; ++j) {
-          const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
-          if (j == jslot) {
-            const float w = lt * fast_exp2(mt - M);
-            Ls += w;
+          for (int nb = 0; nb < NB; ++nb) oo[nb] = ld_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u);
+          const float m0 = jslot == 0 ? mt : mo, m1 = jslot == 0 ? mo : mt;
+          const float l0 = jslot == 0 ? lt : lo, l1 = jslot == 0 ? lo : lt;
+          const float M = fmaxf(fmaxf(kNoMax, m0), m1);
+          const float w0 = l0 * fast_exp2(m0 - M), w1 = l1 * fast_exp2(m1 - M);
+          float Ls = 0.f;
+          Ls += w0;
+          Ls += w1;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[nb] += w * (st.o[sl][nb] * inv);
-          } else {
-            const float w = ld_coh1(rm, srow * 8u + 4u) * fast_exp2(ld_coh1(rm, srow * 8u) - M);
-            Ls += w;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[nb] += w * ld_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u);
+          for (int nb = 0; nb < NB; ++nb) {
+            const f32x4 own = st.o[sl][nb] * inv;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc += w0 * (jslot == 0 ? own : oo[nb]);
+            acc += w1 * (jslot == 0 ? oo[nb] : own);
+            store_out4(p, orow * D + nb * 16 + lg * 4, acc * (1.f / Ls));
           }
-        }
+          if (lg == 0) store_ml(p, orow, M, Ls);
+        } else {
+          float M = kNoMax;
+          for (int j = 0; j < E; ++j) {
+            const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
+            M = fmaxf(M, j == jslot ? mt : ld_coh1(rm, srow * 8u));
+          }
+          float Ls = 0.f;
+          f32x4 acc[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, acc[nb] * (1.f / Ls));
-        if (lg == 0) store_ml(p, orow, M, Ls);
+          for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < E; ++j) {
+            const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
+            if (j == jslot) {
+              const float w = lt * fast_exp2(mt - M);
+              Ls += w;
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) acc[nb] += w * (st.o[sl][nb] * inv);
+            } else {
+              const float w = ld_coh1(rm, srow * 8u + 4u) * fast_exp2(ld_coh1(rm, srow * 8u) - M);
+              Ls += w;
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) acc[nb] += w * ld_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u);
+            }
+          }
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, acc[nb] * (1.f / Ls));
+          if (lg == 0) store_ml(p, orow, M, Ls);
+        }
       } else {
         const uint32_t srow = (uint32_t)(((p.slot_off[qi] + jslot) * p.hkv + kvh) * R + hh);
 #pragma unroll

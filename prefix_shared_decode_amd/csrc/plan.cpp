@@ -204,7 +204,10 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
         for (int kvh = 0; kvh < hkv; ++kvh) {
           for (int64_t rb = 0; rb < rows; rb += per) {
             const int64_t rc = std::min(per, rows - rb);
-            WorkItem it{(int32_t)(ITEM_PREFIX_MFMA | (ch << 8)), kvh, g, tb, te, pbase, (int32_t)rb, (int32_t)rc};
+            // a = first row counted over the whole member array, so the tile finds
+            // its queries without reading the group's member offset first
+            WorkItem it{(int32_t)(ITEM_PREFIX_MFMA | (ch << 8)), kvh, g, tb, te, pbase,
+                        (int32_t)(member_off[g] * r + rb), (int32_t)rc};
             const double fl = (double)round_up(te - tb, 64) * round_up(rc, 16) * d * 4;
             mfma.push_back({it, fixed + std::max(fl / mfma_slot, 4.0 * kv_bytes / bw_wave)});
             mfma_set.push_back(((int64_t)g * nchunks + ch) * hkv + kvh);

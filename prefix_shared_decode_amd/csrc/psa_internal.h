@@ -25,7 +25,7 @@ struct WorkItem {
   int32_t tok_begin;  // token range inside the segment; tok_begin is page aligned
   int32_t tok_end;
   int32_t page_base;  // index in the page array of the page holding tok_begin
-  int32_t a;          // MFMA: first row (row = member * r + head_in_group); mat-vec: partials of the query
+  int32_t a;          // MFMA: first row (row = (member_off[group] + member) * r + head); mat-vec: partials of the query
   int32_t b;          // MFMA: rows; mat-vec: partial slot ((slot_off + j) * hkv + kvh), -1 = write out
 };
 static_assert(sizeof(WorkItem) == 32, "WorkItem must stay 32 bytes");

@@ -83,8 +83,10 @@ def _coverage(wl, plan):
         elif kind == 2:
             assert a % r == 0 and bb % r == 0 and 0 < bb <= 128
             assert pbase == b["group_page_off"][ident] + tb // 16
+            first = sum(len(members.get(g2, [])) for g2 in range(ident))  # the group's first member, over all groups
+            assert first * r <= a and a + bb <= (first + len(members[ident])) * r
             for mi in range(a // r, (a + bb) // r):
-                cov.setdefault((members[ident][mi], kvh), []).append(("p", tb, te, kind_full >> 8, None))
+                cov.setdefault((members[ident][mi - first], kvh), []).append(("p", tb, te, kind_full >> 8, None))
         elif kind == 3:
             for kvh2 in range(wl.num_kv_heads):
                 cov.setdefault((ident, kvh2), []).append(("e", 0, 0, 0, None))
