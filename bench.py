@@ -172,6 +172,73 @@ def trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, path):
     log(f"trace span {res['span_us']:.1f} us")
 
 
+def timed(fn, steps, flush, sink):
+    """Mean ms of fn() over `steps` runs, HIP events around each run, caches
+    flushed (by a read) before each."""
+    import numpy as np
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            torch.sum(flush, dim=None, out=sink)
+        evs[i][0].record()
+        fn()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def components(P, cfg, batch, wl, q, k, v, flush, sink, steps, fused_ms):
+    """The fused launch's two halves alone, and the unfused structure the pages
+    describe as prior work: a prefix launch, a distinct launch and a merge
+    launch (three launches, partials through HBM)."""
+    import torch
+
+    n = len(batch["query_group"])
+    res = {}
+    parts = {}
+    for name, flag in (("prefix_only", P.PREFIX_ONLY), ("distinct_only", P.DISTINCT_ONLY)):
+        plan = P.psa_build_plan(cfg, batch, flags=flag)
+        info = plan.info()
+        ws = torch.empty(max(int(info["workspace_bytes"]), 256), dtype=torch.uint8, device="cuda")
+        P.psa_plan_upload(plan, ws)
+        o = torch.empty((n, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+        m = torch.empty((n, wl.num_q_heads), dtype=torch.float32, device="cuda")
+        l = torch.empty_like(m)
+        torch.cuda.synchronize()
+        parts[name] = (plan, ws, o, m, l, info)
+        ms = timed(lambda: P.psa_decode_attention(plan, q, k, v, o, ws, m, l), steps, flush, sink)
+        rec = {"ms": ms}
+        if name == "prefix_only":
+            tf = info["prefix_flops"] / (ms / 1e3) / 1e12
+            rec.update({"prefix_tflops": tf, "mfma_peak_tflops": BF16_MFMA_PEAK_TFLOPS, "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS,
+                        "note": "prefix flops (4 d Hq per attended prefix token) over the launch time; the launch "
+                                "also writes the prefix partials"})
+        else:
+            gbps = info["distinct_kv_bytes"] / (ms / 1e3) / 1e9
+            alg = info["algorithmic_bytes"] / (ms / 1e3) / 1e9  # distinct KV + q + out of this launch
+            rec.update({"distinct_kv_GBps": gbps, "algorithmic_GBps": alg, "hbm_frac": alg / HBM_PEAK_GBPS})
+        res[name] = rec
+    (pa, wa, oa, ma, la, _), (pb, wb, ob, mb, lb, _) = parts["prefix_only"], parts["distinct_only"]
+    o = torch.empty_like(oa)
+    m = torch.empty_like(ma)
+    l = torch.empty_like(la)
+    d = wl.head_dim
+
+    def unfused():
+        P.psa_decode_attention(pa, q, k, v, oa, wa, ma, la)
+        P.psa_decode_attention(pb, q, k, v, ob, wb, mb, lb)
+        P.psa_merge(oa.view(-1, d), ma.view(-1), la.view(-1), ob.view(-1, d), mb.view(-1), lb.view(-1),
+                    o.view(-1, d), m.view(-1), l.view(-1))
+
+    ms = timed(unfused, steps, flush, sink)
+    res["unfused_3_launches"] = {"ms": ms, "fused_speedup": ms / fused_ms}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +257,8 @@ def main():
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--trace", default=None,
                     help="after timing, run one traced launch and write its per-unit timeline summary (JSON) here")
+    ap.add_argument("--no-components", action="store_true",
+                    help="skip the prefix-only / distinct-only / unfused three-launch measurements")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (counter calibration)")
     args = ap.parse_args()
@@ -304,6 +373,8 @@ def main():
     }
     if info["prefix_flops"] > 0:
         rec["roofline"]["prefix_flops_per_launch"] = info["prefix_flops"]
+    if not args.no_components and args.flags == 0 and info["num_prefix_items"] > 0:
+        rec["components"] = components(P, cfg, batch, wl, q, k, v, flush, sink, max(10, args.steps // 2), ms)
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle on a sample")
         rec["cpu_baseline"] = cpu_baseline(wl, batch, q, k, v, args.cpu_seconds, 30.0)
