@@ -882,120 +882,151 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
   else
     run(std::integral_constant<int, 0>{});
 
-  // ---- write each row's partial (or the output when the chunk is all of it) ----
+  // ---- per row: the output (the chunk is the whole context), a merge in
+  // registers (every other piece of the (query, kv head) had arrived when the
+  // last block started), or a partial and an arrival.  Both slices' memory
+  // operations are issued together, so the epilogue costs few round trips.
   const auto ro = make_rsrc(p.part_o, p.part_o_bytes);
   const auto rm = make_rsrc(p.part_ml, p.part_ml_bytes);
+  bool valid[2], head[2];
+  int qi[2], hh[2], E[2], dec[2];
+  float inv[2], mt[2], lt[2];
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
-    if (sl >= ns) continue;
+    valid[sl] = head[sl] = false;
+    qi[sl] = hh[sl] = dec[sl] = 0;
+    E[sl] = 1;
+    inv[sl] = mt[sl] = lt[sl] = 0.f;
+    if (sl >= ns) continue;  // wave-uniform
     float L = st.lrow[sl], L0, L1;
     lane_pair<32>(L, L0, L1);
     L = L0 + L1;
     lane_pair<16>(L, L0, L1);
     L = L0 + L1;
     const float Lr = st.rsum[sl][0];  // every element holds the row's sum
-    st.mtrue[sl] = max_lane_groups(st.mtrue[sl]);
+    mt[sl] = max_lane_groups(st.mtrue[sl]);
     const int row = (wave + kWaves * sl) * 16 + l16;
-    const bool valid = row < rc;
-    const int grow = rb + row;  // a query's R rows lie in one slice (R divides 16)
-    const int qi = valid ? qrow[sl] : 0, hh = grow % R;
-    const float inv = 1.f / Lr;  // normalise with the sum of the rounded weights used in P.V
-    const float mt = st.mtrue[sl];
-    const float lt = L * fast_exp2(st.mref[sl] - mt);
-    const int E = p.expected[qi];
-    const int64_t orow = (int64_t)qi * p.hq + kvh * R + hh;
-    int32_t* ctr = p.counters + (int64_t)qi * p.hkv + kvh;
-    // One lane per (query, kv head) has read its arrival counter: when all
-    // the other pieces had arrived, this tile is the last one and merges in
-    // registers (dec 1); otherwise it writes a partial and arrives (dec 2).
-    const bool head = valid && lg == 0 && hh == 0;
-    int dec = 0;
-    if (head && E > 1) dec = cval[sl] == E - 1 ? 1 : 2;
-    dec = __shfl(dec, l16 - hh);  // the query's head-0 row, lane group 0
-    if (valid) {
-      if (E == 1) {
+    valid[sl] = row < rc;
+    hh[sl] = (rb + row) % R;  // a query's R rows lie in one slice (R divides 16)
+    qi[sl] = valid[sl] ? qrow[sl] : 0;
+    inv[sl] = 1.f / Lr;  // normalise with the sum of the rounded weights used in P.V
+    lt[sl] = L * fast_exp2(st.mref[sl] - mt[sl]);
+    E[sl] = valid[sl] ? p.expected[qi[sl]] : 1;
+    // the head-0 lane of each query has read the arrival counter: 1 = every
+    // other piece had arrived (merge here), 2 = write a partial and arrive
+    head[sl] = valid[sl] && lg == 0 && hh[sl] == 0;
+    int d = 0;
+    if (head[sl] && E[sl] > 1) d = cval[sl] == E[sl] - 1 ? 1 : 2;
+    dec[sl] = __shfl(d, l16 - hh[sl]);  // the query's head-0 row, lane group 0
+  }
+  // Partials first: their stores must be complete before the arrival, and
+  // the arrivals' round trip then overlaps the loads of the merges below.
+  bool wrote = false;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, st.o[sl][nb] * inv);
-        if (lg == 0) store_ml(p, orow, mt, lt);
-      } else if (dec == 1) {
-        // the merge of the E partials in slot order, with the operations of
-        // merge_wave (uncontracted), this tile's own partial (slot jslot)
-        // taken from registers
+  for (int sl = 0; sl < 2; ++sl) {
+    if (!(valid[sl] && E[sl] > 1 && dec[sl] == 2)) continue;
+    wrote = true;
+    const uint32_t srow = (uint32_t)(((p.slot_off[qi[sl]] + jslot) * p.hkv + kvh) * R + hh[sl]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) st_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u, st.o[sl][nb] * inv[sl]);
+    if (lg == 0) {
+      st_coh1(rm, srow * 8u, mt[sl]);
+      st_coh1(rm, srow * 8u + 4u, lt[sl]);
+    }
+  }
+  const bool any_partial = __builtin_amdgcn_ballot_w64(wrote) != 0;
+  if (any_partial) release_partials();
+  // arrivals (one wave holds all rows of a query); counters of pairs merged
+  // here go back to zero (no other piece touches them in this launch)
+  int old[2] = {0, 0};
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    int32_t* ctr = p.counters + (int64_t)qi[sl] * p.hkv + kvh;
+    if (head[sl] && dec[sl] == 1) reset_counter(ctr);
+    if (head[sl] && dec[sl] == 2) old[sl] = arrive_counter(ctr);
+  }
+  // the other piece of two-piece merges, both slices at once
+  f32x4 oo[2][NB];
+  float mo[2] = {0.f, 0.f}, lo[2] = {0.f, 0.f};
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    if (!(valid[sl] && E[sl] == 2 && dec[sl] == 1)) continue;
+    const uint32_t srow = (uint32_t)(((p.slot_off[qi[sl]] + (1 - jslot)) * p.hkv + kvh) * R + hh[sl]);
+    mo[sl] = ld_coh1(rm, srow * 8u);
+    lo[sl] = ld_coh1(rm, srow * 8u + 4u);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) oo[sl][nb] = ld_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u);
+  }
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    if (!valid[sl]) continue;
+    const int64_t orow = (int64_t)qi[sl] * p.hq + kvh * R + hh[sl];
+    if (E[sl] == 1) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, st.o[sl][nb] * inv[sl]);
+      if (lg == 0) store_ml(p, orow, mt[sl], lt[sl]);
+    } else if (dec[sl] == 1) {
+      // the merge of the E partials in slot order, with the operations of
+      // merge_wave (uncontracted), this tile's own partial (slot jslot) taken
+      // from registers
 #pragma clang fp contract(off)
-        const int64_t s0 = p.slot_off[qi];
-        if (E == 2) {  // one other piece: its m, l and O in one round trip
-          const int jo = 1 - jslot;
-          const uint32_t srow = (uint32_t)(((s0 + jo) * p.hkv + kvh) * R + hh);
-          const float mo = ld_coh1(rm, srow * 8u), lo = ld_coh1(rm, srow * 8u + 4u);
-          f32x4 oo[NB];
+      if (E[sl] == 2) {
+        const float m0 = jslot == 0 ? mt[sl] : mo[sl], m1 = jslot == 0 ? mo[sl] : mt[sl];
+        const float l0 = jslot == 0 ? lt[sl] : lo[sl], l1 = jslot == 0 ? lo[sl] : lt[sl];
+        const float M = fmaxf(fmaxf(kNoMax, m0), m1);
+        const float w0 = l0 * fast_exp2(m0 - M), w1 = l1 * fast_exp2(m1 - M);
+        float Ls = 0.f;
+        Ls += w0;
+        Ls += w1;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) oo[nb] = ld_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u);
-          const float m0 = jslot == 0 ? mt : mo, m1 = jslot == 0 ? mo : mt;
-          const float l0 = jslot == 0 ? lt : lo, l1 = jslot == 0 ? lo : lt;
-          const float M = fmaxf(fmaxf(kNoMax, m0), m1);
-          const float w0 = l0 * fast_exp2(m0 - M), w1 = l1 * fast_exp2(m1 - M);
-          float Ls = 0.f;
-          Ls += w0;
-          Ls += w1;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const f32x4 own = st.o[sl][nb] * inv;
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc += w0 * (jslot == 0 ? own : oo[nb]);
-            acc += w1 * (jslot == 0 ? oo[nb] : own);
-            store_out4(p, orow * D + nb * 16 + lg * 4, acc * (1.f / Ls));
-          }
-          if (lg == 0) store_ml(p, orow, M, Ls);
-        } else {
-          float M = kNoMax;
-          for (int j = 0; j < E; ++j) {
-            const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
-            M = fmaxf(M, j == jslot ? mt : ld_coh1(rm, srow * 8u));
-          }
-          float Ls = 0.f;
-          f32x4 acc[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int j = 0; j < E; ++j) {
-            const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh);
-            if (j == jslot) {
-              const float w = lt * fast_exp2(mt - M);
-              Ls += w;
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb) acc[nb] += w * (st.o[sl][nb] * inv);
-            } else {
-              const float w = ld_coh1(rm, srow * 8u + 4u) * fast_exp2(ld_coh1(rm, srow * 8u) - M);
-              Ls += w;
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb) acc[nb] += w * ld_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u);
-            }
-          }
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, acc[nb] * (1.f / Ls));
-          if (lg == 0) store_ml(p, orow, M, Ls);
+        for (int nb = 0; nb < NB; ++nb) {
+          const f32x4 own = st.o[sl][nb] * inv[sl];
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc += w0 * (jslot == 0 ? own : oo[sl][nb]);
+          acc += w1 * (jslot == 0 ? oo[sl][nb] : own);
+          store_out4(p, orow * D + nb * 16 + lg * 4, acc * (1.f / Ls));
         }
+        if (lg == 0) store_ml(p, orow, M, Ls);
       } else {
-        const uint32_t srow = (uint32_t)(((p.slot_off[qi] + jslot) * p.hkv + kvh) * R + hh);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) st_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u, st.o[sl][nb] * inv);
-        if (lg == 0) {
-          st_coh1(rm, srow * 8u, mt);
-          st_coh1(rm, srow * 8u + 4u, lt);
+        const int64_t s0 = p.slot_off[qi[sl]];
+        float M = kNoMax;
+        for (int j = 0; j < E[sl]; ++j) {
+          const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh[sl]);
+          M = fmaxf(M, j == jslot ? mt[sl] : ld_coh1(rm, srow * 8u));
         }
+        float Ls = 0.f;
+        f32x4 acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < E[sl]; ++j) {
+          const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh[sl]);
+          if (j == jslot) {
+            const float w = lt[sl] * fast_exp2(mt[sl] - M);
+            Ls += w;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] += w * (st.o[sl][nb] * inv[sl]);
+          } else {
+            const float w = ld_coh1(rm, srow * 8u + 4u) * fast_exp2(ld_coh1(rm, srow * 8u) - M);
+            Ls += w;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] += w * ld_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u);
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, acc[nb] * (1.f / Ls));
+        if (lg == 0) store_ml(p, orow, M, Ls);
       }
     }
-    if (head && dec == 1) reset_counter(ctr);  // no other piece touches it in this launch
-    // arrivals of the partials written above (one wave holds all rows of a
-    // query); the last arrivers merge
-    if (__builtin_amdgcn_ballot_w64(dec == 2)) {
-      release_partials();
-      bool last = false;
-      if (head && dec == 2) last = arrive_counter(ctr) == E - 1;
-      uint64_t lm = __builtin_amdgcn_ballot_w64(last);
+  }
+  // the last arrivers among the partials written above merge
+  if (any_partial) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      uint64_t lm = __builtin_amdgcn_ballot_w64(head[sl] && dec[sl] == 2 && old[sl] == E[sl] - 1);
       while (lm) {
         const int src = __builtin_ctzll(lm);
         lm &= lm - 1;
-        const int q = __builtin_amdgcn_readlane(qi, src);
+        const int q = __builtin_amdgcn_readlane(qi[sl], src);
         merge_wave<D, R>(p, q, kvh);
         if (lane == 0) reset_counter(p.counters + (int64_t)q * p.hkv + kvh);
       }
