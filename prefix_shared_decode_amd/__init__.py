@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     FORCE_MATVEC,
     LIB_PATH,
+    NO_TILE_PAIRS,
     NO_XCD_ORDER,
     PREFIX_ONLY,
     PSA_BF16,

@@ -171,8 +171,8 @@ def test_xcd_order_keeps_prefix_sets_on_one_xcd():
     assert len(pos) == 64 and all(len(v) == 4 for v in pos.values())
     for v in pos.values():
         assert len({x % 8 for x in v}) == 1
-    # longest first: all MFMA units come before the mat-vec units
-    kinds = it[::4, 0] & 0xFF
+    # longest first (without tile pairs): all MFMA units come before the mat-vec units
+    kinds = P.psa_build_plan(_cfg(wl), wl.batch, flags=P.NO_TILE_PAIRS).items()[::4, 0] & 0xFF
     assert kinds[:256].tolist() == [2] * 256 and set(kinds[256:].tolist()) == {1}
     # a smaller explicit chunk splits each set's prefix
     it = P.psa_build_plan(_cfg(wl), wl.batch, prefix_chunk_tokens=1024).items()
@@ -353,3 +353,22 @@ def test_flatten_error_paths():
         cyc = dict(t, node_parent=[1, 0] + list(t["node_parent"][2:]))
         assert _status(lambda: P.psa_flatten_prefix_tree(cyc)) == "PSA_ERR_INVALID_ARGUMENT"
     assert _status(lambda: P.psa_flatten_prefix_tree(t, page_size=8)) == "PSA_ERR_UNSUPPORTED"
+
+
+def test_mfma_tiles_start_two_to_a_cu():
+    """On the 8x100 shape, each XCD queue (units i with i % 8 == x) holds its
+    32 MFMA tiles at local positions [0, 16) and [32, 48): positions k and
+    k + 32 start on the same CU.  Without pairing they lead the queue.  Both
+    orders cover every (query, kv head) exactly."""
+    from workloads import make_workload
+
+    wl = make_workload("llama3_8b_8x100")
+    for flags, want in ((0, list(range(16)) + list(range(32, 48))), (P.NO_TILE_PAIRS, list(range(32)))):
+        plan = P.psa_build_plan(_cfg(wl), wl.batch, flags=flags)
+        items = plan.items()
+        kinds = items[::4, 0] & 0xFF
+        for x in range(8):
+            local = kinds[x::8]
+            assert list(np.nonzero(local == 2)[0]) == want, (flags, x)
+        _check_coverage(wl, plan)
+
