@@ -365,6 +365,17 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
   // the first page's wave-wide max per head.  A later score above it by more
   // than kSlack flags the item, which is then redone with the exact maximum
   // found by the first pass (so it cannot be exceeded).
+  // The arrival counter of (query, kv head) is read while the last pages are
+  // processed: if every other piece has arrived by then, this wave merges in
+  // registers at the end instead of writing a partial.
+  const int E = it.a, slot = it.b;
+  int32_t* ctr = p.counters + (int64_t)qi * p.hkv + kvh;
+  int cval = -1;
+  bool ctr_read = E < 2;
+  auto read_ctr = [&]() {
+    cval = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ctr_read = true;
+  };
   bool fixed_ref = false;
   for (int attempt = 0; attempt < 2; ++attempt) {
 #pragma unroll
@@ -398,6 +409,7 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
     }
     load(b[0], kMvPages);
     for (int j = 1; j < npages; j += kMvPages) {
+      if (!ctr_read && j + kMvPages >= npages) read_ctr();
 #pragma unroll
       for (int u = 0; u < kMvPages; ++u) {
         const int bi = (u + 1) % kMvPages;
@@ -409,6 +421,7 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
         load(b[bi], j + u + kMvPages);
       }
     }
+    if (!ctr_read) read_ctr();
     if (!__builtin_amdgcn_ballot_w64(over)) break;
     // rare: redo with the exact per-head maximum of this chunk
 #pragma unroll
@@ -449,47 +462,110 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
   merge_step(std::integral_constant<int, 16>{});
   merge_step(std::integral_constant<int, 32>{});
 
-  // lanes 0..LPT-1 write: O normalised, m (true max), l relative to it
-  const int E = it.a, slot = it.b;
-  if (ts == 0) {
+  // lanes 0..LPT-1 hold the result: O normalised, m (true max), l relative to it
+  float inv[R], lt[R];
 #pragma unroll
-    for (int h = 0; h < R; ++h) {
-      const float inv = 1.f / l[h];
-      const float lt = l[h] * fast_exp2(mref[h] - mtrue[h]);
-      const int64_t row = (int64_t)qi * p.hq + kvh * R + h;
+  for (int h = 0; h < R; ++h) {
+    inv[h] = 1.f / l[h];
+    lt[h] = l[h] * fast_exp2(mref[h] - mtrue[h]);
+  }
+  const bool last_by_count = E > 1 && __builtin_amdgcn_readfirstlane(cval) == E - 1;
+  if (E == 1 || last_by_count) {
+    if (ts == 0) {
       if (E == 1) {
 #pragma unroll
-        for (int k = 0; k < NCH; ++k)
+        for (int h = 0; h < R; ++h) {
+          const int64_t row = (int64_t)qi * p.hq + kvh * R + h;
 #pragma unroll
-          for (int q4 = 0; q4 < EPC / 4; ++q4) {
-            const int e = k * EPC + q4 * 4;
-            f32x4 v = {o[h][e] * inv, o[h][e + 1] * inv, o[h][e + 2] * inv, o[h][e + 3] * inv};
-            store_out4(p, row * D + (k * LPT + c) * EPC + q4 * 4, v);
-          }
-        if (c == 0) store_ml(p, row, mtrue[h], lt);
+          for (int k = 0; k < NCH; ++k)
+#pragma unroll
+            for (int q4 = 0; q4 < EPC / 4; ++q4) {
+              const int e = k * EPC + q4 * 4;
+              f32x4 v = {o[h][e] * inv[h], o[h][e + 1] * inv[h], o[h][e + 2] * inv[h], o[h][e + 3] * inv[h]};
+              store_out4(p, row * D + (k * LPT + c) * EPC + q4 * 4, v);
+            }
+          if (c == 0) store_ml(p, row, mtrue[h], lt[h]);
+        }
       } else {
+        // every other piece had arrived: the merge of the E partials in slot
+        // order with the operations of merge_wave (uncontracted), this
+        // wave's own partial (slot jown) taken from registers
+#pragma clang fp contract(off)
         const auto ro = make_rsrc(p.part_o, p.part_o_bytes);
-        const uint32_t srow = (uint32_t)(slot * R + h);
+        const auto rm = make_rsrc(p.part_ml, p.part_ml_bytes);
+        const int64_t s0 = p.slot_off[qi];
+        const int jown = slot / p.hkv - (int)s0;
 #pragma unroll
-        for (int k = 0; k < NCH; ++k)
-#pragma unroll
-          for (int q4 = 0; q4 < EPC / 4; ++q4) {
-            const int e = k * EPC + q4 * 4;
-            f32x4 v = {o[h][e] * inv, o[h][e + 1] * inv, o[h][e + 2] * inv, o[h][e + 3] * inv};
-            st_coh4(ro, (srow * D + (k * LPT + c) * EPC + q4 * 4) * 4u, v);
+        for (int h = 0; h < R; ++h) {
+          const int64_t row = (int64_t)qi * p.hq + kvh * R + h;
+          float M = kNoMax;
+          for (int j = 0; j < E; ++j) {
+            const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
+            M = fmaxf(M, j == jown ? mtrue[h] : ld_coh1(rm, srow * 8u));
           }
-        if (c == 0) {
-          const auto rm = make_rsrc(p.part_ml, p.part_ml_bytes);
-          st_coh1(rm, srow * 8u, mtrue[h]);
-          st_coh1(rm, srow * 8u + 4u, lt);
+          float Ls = 0.f;
+          f32x4 acc[NCH * EPC / 4];
+#pragma unroll
+          for (int a4 = 0; a4 < NCH * EPC / 4; ++a4) acc[a4] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < E; ++j) {
+            const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
+            if (j == jown) {
+              const float w = lt[h] * fast_exp2(mtrue[h] - M);
+              Ls += w;
+#pragma unroll
+              for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                for (int q4 = 0; q4 < EPC / 4; ++q4) {
+                  const int e = k * EPC + q4 * 4;
+                  const f32x4 own = {o[h][e] * inv[h], o[h][e + 1] * inv[h], o[h][e + 2] * inv[h],
+                                     o[h][e + 3] * inv[h]};
+                  acc[k * (EPC / 4) + q4] += w * own;
+                }
+            } else {
+              const float w = ld_coh1(rm, srow * 8u + 4u) * fast_exp2(ld_coh1(rm, srow * 8u) - M);
+              Ls += w;
+#pragma unroll
+              for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                for (int q4 = 0; q4 < EPC / 4; ++q4)
+                  acc[k * (EPC / 4) + q4] += w * ld_coh4(ro, (srow * D + (k * LPT + c) * EPC + q4 * 4) * 4u);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < NCH; ++k)
+#pragma unroll
+            for (int q4 = 0; q4 < EPC / 4; ++q4)
+              store_out4(p, row * D + (k * LPT + c) * EPC + q4 * 4, acc[k * (EPC / 4) + q4] * (1.f / Ls));
+          if (c == 0) store_ml(p, row, M, Ls);
         }
       }
     }
+    if (E > 1 && lane == 0) reset_counter(ctr);  // no other piece touches it in this launch
+    return;
   }
-  if (E == 1) return;
+  // a partial, then the arrival; the last arriver merges
+  if (ts == 0) {
+    const auto ro = make_rsrc(p.part_o, p.part_o_bytes);
+    const auto rm = make_rsrc(p.part_ml, p.part_ml_bytes);
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      const uint32_t srow = (uint32_t)(slot * R + h);
+#pragma unroll
+      for (int k = 0; k < NCH; ++k)
+#pragma unroll
+        for (int q4 = 0; q4 < EPC / 4; ++q4) {
+          const int e = k * EPC + q4 * 4;
+          f32x4 v = {o[h][e] * inv[h], o[h][e + 1] * inv[h], o[h][e + 2] * inv[h], o[h][e + 3] * inv[h]};
+          st_coh4(ro, (srow * D + (k * LPT + c) * EPC + q4 * 4) * 4u, v);
+        }
+      if (c == 0) {
+        st_coh1(rm, srow * 8u, mtrue[h]);
+        st_coh1(rm, srow * 8u + 4u, lt[h]);
+      }
+    }
+  }
   release_partials();
   int old = 0;
-  int32_t* ctr = p.counters + (int64_t)qi * p.hkv + kvh;
   if (lane == 0) old = arrive_counter(ctr);
   old = __builtin_amdgcn_readfirstlane(old);
   if (old == E - 1) {
