@@ -219,7 +219,8 @@ def components(P, cfg, batch, wl, q, k, v, flush, sink, steps, fused_ms):
                                 "also writes the prefix partials"})
         else:
             gbps = info["distinct_kv_bytes"] / (ms / 1e3) / 1e9
-            alg = info["algorithmic_bytes"] / (ms / 1e3) / 1e9  # distinct KV + q + out of this launch
+            q_out = info["algorithmic_bytes"] - info["prefix_kv_bytes"] - info["distinct_kv_bytes"]
+            alg = (info["distinct_kv_bytes"] + q_out) / (ms / 1e3) / 1e9  # distinct KV + q + out
             rec.update({"distinct_kv_GBps": gbps, "algorithmic_GBps": alg, "hbm_frac": alg / HBM_PEAK_GBPS})
         res[name] = rec
     (pa, wa, oa, ma, la, _), (pb, wb, ob, mb, lb, _) = parts["prefix_only"], parts["distinct_only"]
