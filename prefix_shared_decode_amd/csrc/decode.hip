@@ -109,6 +109,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 #define PSA_MV_PAGES 2
 #endif
 constexpr int kMvPages = PSA_MV_PAGES;  // mat-vec tile: pages of K and V in flight per wave
+constexpr int kMergeUnroll = 4;         // in-register merges of up to this many pieces load in one pass
 constexpr int kSc1 = 16;  // cache policy: coherent at device (agent) scope
 constexpr int kNt = 2;    // cache policy: non-temporal (streamed once; keeps reused prefix K/V and
                           // partials from being evicted by the distinct KV stream)
@@ -495,48 +496,100 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
         const auto rm = make_rsrc(p.part_ml, p.part_ml_bytes);
         const int64_t s0 = p.slot_off[qi];
         const int jown = slot / p.hkv - (int)s0;
+        constexpr int NQ = NCH * EPC / 4;  // float4 chunks of a head this lane holds
+        auto own4 = [&](int h, int k, int q4) {
+          const int e = k * EPC + q4 * 4;
+          return f32x4{o[h][e] * inv[h], o[h][e + 1] * inv[h], o[h][e + 2] * inv[h], o[h][e + 3] * inv[h]};
+        };
+        if (R <= 4 && E <= kMergeUnroll) {
+          // up to kMergeUnroll pieces: every load of a pass in flight together
+          float mj[R][kMergeUnroll], lj[R][kMergeUnroll];
 #pragma unroll
-        for (int h = 0; h < R; ++h) {
-          const int64_t row = (int64_t)qi * p.hq + kvh * R + h;
-          float M = kNoMax;
-          for (int j = 0; j < E; ++j) {
-            const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
-            M = fmaxf(M, j == jown ? mtrue[h] : ld_coh1(rm, srow * 8u));
-          }
-          float Ls = 0.f;
-          f32x4 acc[NCH * EPC / 4];
+          for (int h = 0; h < R; ++h)
 #pragma unroll
-          for (int a4 = 0; a4 < NCH * EPC / 4; ++a4) acc[a4] = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int j = 0; j < E; ++j) {
-            const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
-            if (j == jown) {
-              const float w = lt[h] * fast_exp2(mtrue[h] - M);
-              Ls += w;
+            for (int j = 0; j < kMergeUnroll; ++j) {
+              mj[h][j] = mtrue[h];
+              lj[h][j] = lt[h];
+              if (j < E && j != jown) {
+                const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
+                mj[h][j] = ld_coh1(rm, srow * 8u);
+                lj[h][j] = ld_coh1(rm, srow * 8u + 4u);
+              }
+            }
+          float M[R], Ls[R];
+          f32x4 acc[R][NQ];
 #pragma unroll
-              for (int k = 0; k < NCH; ++k)
+          for (int h = 0; h < R; ++h) {
+            M[h] = kNoMax;
 #pragma unroll
-                for (int q4 = 0; q4 < EPC / 4; ++q4) {
-                  const int e = k * EPC + q4 * 4;
-                  const f32x4 own = {o[h][e] * inv[h], o[h][e + 1] * inv[h], o[h][e + 2] * inv[h],
-                                     o[h][e + 3] * inv[h]};
-                  acc[k * (EPC / 4) + q4] += w * own;
-                }
-            } else {
-              const float w = ld_coh1(rm, srow * 8u + 4u) * fast_exp2(ld_coh1(rm, srow * 8u) - M);
-              Ls += w;
+            for (int j = 0; j < kMergeUnroll; ++j)
+              if (j < E) M[h] = fmaxf(M[h], mj[h][j]);
+            Ls[h] = 0.f;
+#pragma unroll
+            for (int a4 = 0; a4 < NQ; ++a4) acc[h][a4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kMergeUnroll; ++j) {
+              if (j >= E) continue;
+              const float w = lj[h][j] * fast_exp2(mj[h][j] - M[h]);
+              Ls[h] += w;
+              const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
 #pragma unroll
               for (int k = 0; k < NCH; ++k)
 #pragma unroll
                 for (int q4 = 0; q4 < EPC / 4; ++q4)
-                  acc[k * (EPC / 4) + q4] += w * ld_coh4(ro, (srow * D + (k * LPT + c) * EPC + q4 * 4) * 4u);
+                  acc[h][k * (EPC / 4) + q4] +=
+                      w * (j == jown ? own4(h, k, q4) : ld_coh4(ro, (srow * D + (k * LPT + c) * EPC + q4 * 4) * 4u));
             }
           }
 #pragma unroll
-          for (int k = 0; k < NCH; ++k)
+          for (int h = 0; h < R; ++h) {
+            const int64_t row = (int64_t)qi * p.hq + kvh * R + h;
 #pragma unroll
-            for (int q4 = 0; q4 < EPC / 4; ++q4)
-              store_out4(p, row * D + (k * LPT + c) * EPC + q4 * 4, acc[k * (EPC / 4) + q4] * (1.f / Ls));
-          if (c == 0) store_ml(p, row, M, Ls);
+            for (int k = 0; k < NCH; ++k)
+#pragma unroll
+              for (int q4 = 0; q4 < EPC / 4; ++q4)
+                store_out4(p, row * D + (k * LPT + c) * EPC + q4 * 4, acc[h][k * (EPC / 4) + q4] * (1.f / Ls[h]));
+            if (c == 0) store_ml(p, row, M[h], Ls[h]);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < R; ++h) {
+            const int64_t row = (int64_t)qi * p.hq + kvh * R + h;
+            float M = kNoMax;
+            for (int j = 0; j < E; ++j) {
+              const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
+              M = fmaxf(M, j == jown ? mtrue[h] : ld_coh1(rm, srow * 8u));
+            }
+            float Ls = 0.f;
+            f32x4 acc[NQ];
+#pragma unroll
+            for (int a4 = 0; a4 < NQ; ++a4) acc[a4] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < E; ++j) {
+              const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
+              if (j == jown) {
+                const float w = lt[h] * fast_exp2(mtrue[h] - M);
+                Ls += w;
+#pragma unroll
+                for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                  for (int q4 = 0; q4 < EPC / 4; ++q4) acc[k * (EPC / 4) + q4] += w * own4(h, k, q4);
+              } else {
+                const float w = ld_coh1(rm, srow * 8u + 4u) * fast_exp2(ld_coh1(rm, srow * 8u) - M);
+                Ls += w;
+#pragma unroll
+                for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                  for (int q4 = 0; q4 < EPC / 4; ++q4)
+                    acc[k * (EPC / 4) + q4] += w * ld_coh4(ro, (srow * D + (k * LPT + c) * EPC + q4 * 4) * 4u);
+              }
+            }
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+#pragma unroll
+              for (int q4 = 0; q4 < EPC / 4; ++q4)
+                store_out4(p, row * D + (k * LPT + c) * EPC + q4 * 4, acc[k * (EPC / 4) + q4] * (1.f / Ls));
+            if (c == 0) store_ml(p, row, M, Ls);
+          }
         }
       }
     }
@@ -614,6 +667,14 @@ constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF0
 // explicitly with s_waitcnt vmcnt, followed by a barrier.  The LDS pointer is
 // an operand so that the compiler knows the stage may change.
 __device__ __forceinline__ void copy_to_lds(const char* gbase, uint32_t voff, lds_char* lds) {
+  // both bases are wave-uniform; say so, so that they are in scalar registers
+  // whatever the register allocator did with the arithmetic that made them
+  // (readfirstlane yields a signed int: widen each half as unsigned)
+  const uint64_t gb = reinterpret_cast<uint64_t>(gbase);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gb);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(gb >> 32));
+  gbase = reinterpret_cast<const char*>(((uint64_t)hi << 32) | (uint64_t)lo);
+  lds = (lds_char*)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   int saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
