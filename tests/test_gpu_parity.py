@@ -50,6 +50,8 @@ SMALL = {
     "d64_r8": dict(hq=16, hkv=2, d=64, groups=[(130, 6, (0, 70))], ung=(2, (1, 40))),
     # GQA ratio 2 with a group just above the MFMA threshold
     "r2_tail_rows": dict(hq=8, hkv=4, d=128, groups=[(33, 9, (0, 20))], ung=(1, (1, 17))),
+    # GQA ratio 8 at head_dim 128 (64 query heads over 8 kv heads)
+    "gqa8_d128": dict(hq=64, hkv=8, d=128, groups=[(260, 10, (0, 120)), (40, 3, (1, 30))], ung=(2, (1, 200))),
 }
 
 
