@@ -191,7 +191,45 @@ def timed(fn, steps, flush, sink):
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def components(P, cfg, batch, wl, q, k, v, flush, sink, steps, fused_ms):
+def measured_peaks(P, buf, reps):
+    """Measured ceilings of this GPU (psa_debug_read_peak / psa_debug_mfma_peak):
+    the best of `reps` launches of a 1 GiB streaming read, and of a dependent
+    bf16 MFMA run at eight waves per CU."""
+    import torch
+
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+    fout = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    nbytes = buf.numel() * buf.element_size()
+    iters = 4096
+    flops = 0.0
+
+    def rd():
+        P.psa_debug_read_peak(buf, sink)
+
+    def mf():
+        nonlocal flops
+        flops = P.psa_debug_mfma_peak(fout, iters)
+
+    best = {}
+    for name, fn in (("read", rd), ("mfma", mf)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        best[name] = min(ts)
+    return {"hbm_read_GBps": nbytes / (best["read"] / 1e3) / 1e9, "read_bytes": nbytes,
+            "mfma_bf16_TFLOPs": flops / (best["mfma"] / 1e3) / 1e12,
+            "note": "best of %d launches each: a non-temporal 16-byte-load read of %d MiB (one contiguous span per workgroup), and 2048x4 waves of "
+                    "%d dependent v_mfma_f32_16x16x32_bf16" % (reps, nbytes >> 20, iters)}
+
+
+def components(P, cfg, batch, wl, q, k, v, flush, sink, steps, fused_ms, peaks=None):
     """The fused launch's two halves alone, and the unfused structure the pages
     describe as prior work: a prefix launch, a distinct launch and a merge
     launch (three launches, partials through HBM)."""
@@ -214,6 +252,8 @@ def components(P, cfg, batch, wl, q, k, v, flush, sink, steps, fused_ms):
         rec = {"ms": ms}
         if name == "prefix_only":
             tf = info["prefix_flops"] / (ms / 1e3) / 1e12
+            if peaks:
+                rec["mfma_frac_of_measured"] = tf / peaks["mfma_bf16_TFLOPs"]
             rec.update({"prefix_tflops": tf, "mfma_peak_tflops": BF16_MFMA_PEAK_TFLOPS, "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS,
                         "note": "prefix flops (4 d Hq per attended prefix token) over the launch time; the launch "
                                 "also writes the prefix partials"})
@@ -222,6 +262,8 @@ def components(P, cfg, batch, wl, q, k, v, flush, sink, steps, fused_ms):
             q_out = info["algorithmic_bytes"] - info["prefix_kv_bytes"] - info["distinct_kv_bytes"]
             alg = (info["distinct_kv_bytes"] + q_out) / (ms / 1e3) / 1e9  # distinct KV + q + out
             rec.update({"distinct_kv_GBps": gbps, "algorithmic_GBps": alg, "hbm_frac": alg / HBM_PEAK_GBPS})
+            if peaks:
+                rec["hbm_frac_of_measured_read"] = alg / peaks["hbm_read_GBps"]
         res[name] = rec
     (pa, wa, oa, ma, la, _), (pb, wb, ob, mb, lb, _) = parts["prefix_only"], parts["distinct_only"]
     o = torch.empty_like(oa)
@@ -258,6 +300,7 @@ def main():
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--trace", default=None,
                     help="after timing, run one traced launch and write its per-unit timeline summary (JSON) here")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured read / MFMA ceilings")
     ap.add_argument("--no-components", action="store_true",
                     help="skip the prefix-only / distinct-only / unfused three-launch measurements")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -374,8 +417,13 @@ def main():
     }
     if info["prefix_flops"] > 0:
         rec["roofline"]["prefix_flops_per_launch"] = info["prefix_flops"]
+    if not args.no_peaks and flush is not None:
+        rec["measured_peaks"] = measured_peaks(P, flush, max(5, args.steps // 5))
+        mp = rec["measured_peaks"]
+        rec["roofline"]["frac_of_measured_read_peak"] = achieved / mp["hbm_read_GBps"]
     if not args.no_components and args.flags == 0 and info["num_prefix_items"] > 0:
-        rec["components"] = components(P, cfg, batch, wl, q, k, v, flush, sink, max(10, args.steps // 2), ms)
+        rec["components"] = components(P, cfg, batch, wl, q, k, v, flush, sink, max(10, args.steps // 2), ms,
+                                       rec.get("measured_peaks"))
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle on a sample")
         rec["cpu_baseline"] = cpu_baseline(wl, batch, q, k, v, args.cpu_seconds, 30.0)

@@ -39,6 +39,25 @@ psa_status psa_decode_attention_traced(const psa_plan* plan, const void* d_q, co
                                        void* d_workspace, size_t bytes, void* d_trace, int64_t trace_capacity,
                                        void* stream);
 
+/* Measured ceilings for the rooflines (diagnostics; attention does not use
+ * them).  Each call enqueues one launch on `stream`; time it with events.
+ *
+ * psa_debug_read_peak: reads `bytes` (a positive multiple of 16, at most
+ * 2 GiB) of device memory d_buf once, with 16-byte non-temporal loads from
+ * 2048 workgroups of 256 threads, and writes one uint32 per thread to d_sink
+ * (sink_capacity >= 2048 * 256 entries) so no load is dead.  Bytes read per
+ * launch = bytes.
+ *
+ * psa_debug_mfma_peak: 2048 workgroups of 4 waves; each wave runs `iters`
+ * (a positive multiple of 8) dependent v_mfma_f32_16x16x32_bf16, and each
+ * thread writes one float to d_out (out_capacity >= 2048 * 256).  Flops per
+ * launch = 2048 * 4 * iters * 16384.
+ *
+ * Errors: NULL or non-device pointers, sizes out of range. */
+psa_status psa_debug_read_peak(const void* d_buf, size_t bytes, uint32_t* d_sink, int64_t sink_capacity,
+                               void* stream);
+psa_status psa_debug_mfma_peak(float* d_out, int64_t out_capacity, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

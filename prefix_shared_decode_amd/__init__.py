@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     lib,
     make_config,
     psa_build_plan,
+    psa_debug_mfma_peak,
+    psa_debug_read_peak,
     psa_decode_attention,
     psa_flatten_prefix_tree,
     psa_merge,

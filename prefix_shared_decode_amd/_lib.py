@@ -25,7 +25,7 @@ STATUS = {0: "PSA_OK", 1: "PSA_ERR_INVALID_ARGUMENT", 2: "PSA_ERR_UNSUPPORTED", 
 EXPORTS = ["psa_build_plan", "psa_plan_get_info", "psa_plan_upload", "psa_decode_attention", "psa_merge",
            "psa_flatten_prefix_tree", "psa_batch_owned_view", "psa_free_batch", "psa_destroy_plan",
            "psa_last_error", "psa_version", "psa_plan_debug_items", "psa_plan_debug_queries",
-           "psa_decode_attention_traced"]
+           "psa_decode_attention_traced", "psa_debug_read_peak", "psa_debug_mfma_peak"]
 
 
 class PsaError(RuntimeError):
@@ -102,6 +102,8 @@ def lib():
         L.psa_plan_debug_items.argtypes = [vp, _I32P, C.c_int64]
         L.psa_plan_debug_queries.argtypes = [vp, _I32P, _I32P, C.c_int64]
         L.psa_decode_attention_traced.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp, C.c_int64, vp]
+        L.psa_debug_read_peak.argtypes = [vp, C.c_size_t, vp, C.c_int64, vp]
+        L.psa_debug_mfma_peak.argtypes = [vp, C.c_int64, C.c_int32, vp]
         for name in EXPORTS:
             fn = getattr(L, name)
             if fn.restype is C.c_int and name not in ("psa_version",):
@@ -266,6 +268,20 @@ def psa_decode_attention(plan, q, k_pool, v_pool, out, workspace, out_m=None, ou
         if trace.dtype != torch.int64:
             raise ValueError("trace: expected an int64 tensor")
         _check(lib().psa_decode_attention_traced(*args, _dev_ptr(trace, "trace"), trace.numel(), _stream_ptr(stream)))
+
+
+def psa_debug_read_peak(buf, sink, stream=None):
+    """One streaming read of device tensor ``buf`` (include/psa_debug.h); ``sink``
+    is a uint32/int32 device tensor of >= 2048 * 256 entries."""
+    _check(lib().psa_debug_read_peak(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), _dev_ptr(sink, "sink"),
+                                     sink.numel(), _stream_ptr(stream)))
+
+
+def psa_debug_mfma_peak(out, iters, stream=None):
+    """One launch of dependent bf16 MFMA chains (include/psa_debug.h); ``out`` is a
+    float32 device tensor of >= 2048 * 256 entries.  Returns the flops it does."""
+    _check(lib().psa_debug_mfma_peak(_dev_ptr(out, "out"), out.numel(), int(iters), _stream_ptr(stream)))
+    return 2048.0 * 4 * iters * 16384
 
 
 def psa_merge(o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, stream=None):

@@ -12,6 +12,8 @@
 namespace psa {
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int r, bool bf16, hipStream_t s);
+hipError_t launch_read_peak(const void* buf, uint32_t bytes, uint32_t* sink, int blocks, hipStream_t s);
+hipError_t launch_mfma_peak(float* out, int iters, int blocks, hipStream_t s);
 hipError_t launch_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* m_a, const float* l_a,
                         const float* o_b, const float* m_b, const float* l_b, float* o, float* m, float* l,
                         hipStream_t s);
@@ -53,6 +55,8 @@ psa_status set_error(psa_status s, const std::string& msg) {
 }  // namespace psa
 
 using psa::set_error;
+
+constexpr int kPeakBlocks = 2048;  // workgroups of the peak kernels: 8 per CU, 4 waves each
 
 extern "C" {
 
@@ -286,6 +290,40 @@ psa_status psa_plan_debug_queries(const psa_plan* plan, int32_t* expected, int32
   if (!plan->expected.empty() && (!expected || !slot_off)) return set_error(PSA_ERR_INVALID_ARGUMENT, "NULL output");
   std::memcpy(expected, plan->expected.data(), plan->expected.size() * 4);
   std::memcpy(slot_off, plan->slot_off.data(), plan->slot_off.size() * 4);
+  return PSA_OK;
+}
+
+psa_status psa_debug_read_peak(const void* d_buf, size_t bytes, uint32_t* d_sink, int64_t sink_capacity,
+                               void* stream) {
+  if (!d_buf || !d_sink) return set_error(PSA_ERR_INVALID_ARGUMENT, "buffer or sink is NULL");
+  if (bytes == 0 || bytes % 16 || bytes > (size_t)1 << 31)
+    return set_error(PSA_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16, at most 2 GiB");
+  if (sink_capacity < (int64_t)kPeakBlocks * 256)
+    return set_error(PSA_ERR_WORKSPACE_TOO_SMALL, "sink needs " + std::to_string(kPeakBlocks * 256) + " entries");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return psa::hip_fail(e, "hipGetDevice");
+  psa_status st = psa::check_device_ptr(d_buf, "buffer", dev);
+  if (st != PSA_OK) return st;
+  st = psa::check_device_ptr(d_sink, "sink", dev);
+  if (st != PSA_OK) return st;
+  e = psa::launch_read_peak(d_buf, (uint32_t)bytes, d_sink, kPeakBlocks, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return psa::hip_fail(e, "read peak kernel launch");
+  return PSA_OK;
+}
+
+psa_status psa_debug_mfma_peak(float* d_out, int64_t out_capacity, int32_t iters, void* stream) {
+  if (!d_out) return set_error(PSA_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (iters <= 0 || iters % 8) return set_error(PSA_ERR_INVALID_ARGUMENT, "iters must be a positive multiple of 8");
+  if (out_capacity < (int64_t)kPeakBlocks * 256)
+    return set_error(PSA_ERR_WORKSPACE_TOO_SMALL, "out needs " + std::to_string(kPeakBlocks * 256) + " entries");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return psa::hip_fail(e, "hipGetDevice");
+  psa_status st = psa::check_device_ptr(d_out, "out", dev);
+  if (st != PSA_OK) return st;
+  e = psa::launch_mfma_peak(d_out, iters, kPeakBlocks, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return psa::hip_fail(e, "mfma peak kernel launch");
   return PSA_OK;
 }
 

@@ -279,3 +279,33 @@ def test_late_dominant_key_triggers_exact_rescaling():
     k[int(gp[380 // 16]), 2, 380 % 16, :] = (12.0 * q[0, 2 * r, :].float()).to(torch.bfloat16)
     _check_full(wl, b, q, k, v, "late dominant key")
     _check_full(wl, b, q, k, v, "late dominant key, mat-vec only", flags=P.FORCE_MATVEC)
+
+
+def test_measured_peak_kernels_run():
+    """The two ceiling kernels run, write every sink entry, and report sane
+    rates (a read well below 8 TB/s is still above 1 TB/s; the MFMA run is
+    above 0.5 PFLOP/s)."""
+    import torch
+
+    buf = torch.ones(64 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.full((2048 * 256,), -1, dtype=torch.int32, device="cuda")
+    out = torch.full((2048 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    log("case measured peak kernels")
+    P.psa_debug_read_peak(buf, sink)
+    flops = P.psa_debug_mfma_peak(out, 256)
+    torch.cuda.synchronize()
+    # bytes of value 1: the xor of an even number of 16-byte chunks per thread
+    assert int((sink == -1).sum()) == 0
+    assert bool(torch.isfinite(out).all())
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    P.psa_debug_read_peak(buf, sink)
+    b.record()
+    b.synchronize()
+    assert buf.numel() / (a.elapsed_time(b) / 1e3) > 1e12
+    a.record()
+    P.psa_debug_mfma_peak(out, 1024)
+    b.record()
+    b.synchronize()
+    assert flops * 4 / (a.elapsed_time(b) / 1e3) > 5e14
+

@@ -372,3 +372,25 @@ def test_mfma_tiles_start_two_to_a_cu():
             assert list(np.nonzero(local == 2)[0]) == want, (flags, x)
         _check_coverage(wl, plan)
 
+
+def test_peak_entry_points_reject_bad_arguments():
+    """Argument checks of psa_debug_read_peak / psa_debug_mfma_peak come before
+    any device access (no GPU needed): NULL pointers, sizes out of range, and
+    too-small sinks are errors with a message."""
+    import ctypes as C
+
+    L = P.lib()
+    fake = C.c_void_p(0x1000)
+    cases = [
+        (L.psa_debug_read_peak, (None, 1 << 20, fake, 2048 * 256, None), "NULL"),
+        (L.psa_debug_read_peak, (fake, 1000, fake, 2048 * 256, None), "multiple of 16"),
+        (L.psa_debug_read_peak, (fake, 3 << 30, fake, 2048 * 256, None), "multiple of 16"),
+        (L.psa_debug_read_peak, (fake, 1 << 20, fake, 100, None), "sink needs"),
+        (L.psa_debug_mfma_peak, (None, 2048 * 256, 64, None), "NULL"),
+        (L.psa_debug_mfma_peak, (fake, 2048 * 256, 12, None), "multiple of 8"),
+        (L.psa_debug_mfma_peak, (fake, 10, 64, None), "out needs"),
+    ]
+    for fn, args, msg in cases:
+        assert fn(*args) != 0
+        assert msg in L.psa_last_error().decode()
+
