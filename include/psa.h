@@ -104,7 +104,7 @@ typedef struct {
 #define PSA_PLAN_FORCE_MATVEC 0x4u  /* no MFMA prefix tiles: every range per query */
 #define PSA_PLAN_DEBUG_POISON 0x8u  /* psa_plan_upload fills partial slots with NaN */
 #define PSA_PLAN_NO_XCD_ORDER 0x10u /* plain longest-first order, no XCD grouping */
-#define PSA_PLAN_NO_TILE_PAIRS 0x20u /* do not start MFMA prefix tiles two to a compute unit */
+#define PSA_PLAN_NO_TILE_PAIRS 0x20u /* MFMA prefix tiles lead each XCD queue (no pairs, no spreading) */
 
 /* Plan options; pass NULL for defaults.  Zero fields take defaults. */
 typedef struct {

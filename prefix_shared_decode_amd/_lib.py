@@ -83,6 +83,12 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise OSError(f"{LIB_PATH} not found: build it with `python -m prefix_shared_decode_amd.build`")
+        # torch brings its own HIP runtime (same soname, libamdhip64.so.7).
+        # Loading it first makes the library bind to that runtime; loaded the
+        # other way round, the process holds two HIP and two HSA runtimes and
+        # the library's finds no device once torch has opened it.
+        import torch  # noqa: F401
+
         L = C.CDLL(LIB_PATH)
         vp = C.c_void_p
         L.psa_build_plan.argtypes = [C.POINTER(psa_config), C.POINTER(psa_batch), C.POINTER(psa_plan_opts),

@@ -323,7 +323,26 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
       for (auto& qq : q) {
         size_t np = 0;
         while (np < qq.size() && units[qq[np]].it[0].kind % 256 == ITEM_PREFIX_MFMA) ++np;
-        if (np < 2 || np > 2 * (size_t)kCusPerXcd || qq.size() < kCusPerXcd + np - (np + 1) / 2) continue;
+        if (np > 2 * (size_t)kCusPerXcd && qq.size() > np) {
+          // More tiles than one round of pairs: spread them evenly through
+          // the queue, so that MFMA tiles (latency bound) and mat-vec units
+          // (HBM bound) run side by side instead of one phase after the
+          // other.  (Measured on the two-level 4x16x16 shape: 0.262 ms
+          // against 0.270 ms with the tiles first; spreading them over the
+          // first 70% only gave 0.266 ms.)
+          const size_t n = qq.size();
+          const size_t span = n;
+          std::vector<int64_t> re;
+          re.reserve(n);
+          size_t mv = np, tk = 0;
+          for (size_t pos = 0; pos < n; ++pos) {
+            const bool tile = tk < np && (mv >= n || tk * span <= pos * np);
+            re.push_back(tile ? qq[tk++] : qq[mv++]);
+          }
+          qq.swap(re);
+          continue;
+        }
+        if (np < 2 || qq.size() < kCusPerXcd + np - (np + 1) / 2) continue;
         const size_t h = (np + 1) / 2;
         std::vector<int64_t> re;
         re.reserve(qq.size());

@@ -14,7 +14,7 @@ import oracle
 import prefix_shared_decode_amd as P
 from workloads import make_values, subset_for_queries
 
-# spec tolerances, over the whole output tensor
+# parity tolerances (bf16 inputs; fp32 inputs), over the whole output tensor
 TOL = {"bf16": {"max_abs": 1e-2, "rel_l2": 5e-3}, "f32": {"max_abs": 1e-5, "rel_l2": 1e-5}}
 
 

@@ -78,6 +78,37 @@ def test_two_level_small_flattened():
     assert_close(to_host64(out), O, "bf16", "two_level_small")
 
 
+def test_library_loaded_before_torch_initialises_the_gpu():
+    """A fresh process whose first call into the library is host-only (the
+    tree flattening) and only then touches the GPU through torch: the binding
+    loads torch's HIP runtime before the library, so both use one runtime."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import numpy as np, oracle, prefix_shared_decode_amd as P\n"
+        "from workloads import build_two_level, make_values\n"
+        "wl = build_two_level('t', 32, 8, 128, 'bf16', 2, 64, 3, 128, 4, (0, 60), seed=5)\n"
+        "batch, _ = P.psa_flatten_prefix_tree(wl.tree)\n"
+        "import torch\n"
+        "q, k, v = make_values(wl, 'cuda')\n"
+        "cfg = P.make_config(32, 8, 128, wl.num_pages, 'bf16', 'f32')\n"
+        "step = P.DecodeStep(cfg, batch)\n"
+        "out = torch.empty((len(batch['query_group']), 32, 128), dtype=torch.float32, device='cuda')\n"
+        "step(q, k, v, out)\n"
+        "torch.cuda.synchronize()\n"
+        "f = lambda t: t.float().cpu().numpy().astype(np.float64)\n"
+        "O, _, _ = oracle.decode_attention(f(q), f(k), f(v), batch)\n"
+        "print('maxerr', float(np.abs(f(out) - O).max()))\n")
+    log("case library loaded before torch initialises the GPU (child process)")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    err = float(r.stdout.split("maxerr")[-1])
+    assert err <= 1e-2, r.stdout
+
+
 # ---------------- edge cases ----------------
 
 def test_stale_padding_is_masked():

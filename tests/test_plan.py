@@ -373,6 +373,38 @@ def test_mfma_tiles_start_two_to_a_cu():
         _check_coverage(wl, plan)
 
 
+def test_mfma_tiles_spread_when_more_than_a_round_of_pairs():
+    """The flattened two-level shape has 128 MFMA tiles per XCD queue (more
+    than two per CU): they are spread evenly through each queue, interleaved
+    with the mat-vec units, instead of leading it; NO_TILE_PAIRS keeps them
+    first.  Both orders cover every (query, kv head) exactly."""
+    from workloads import make_workload
+
+    wl = make_workload("two_level_4x16x16")
+    batch, _ = P.psa_flatten_prefix_tree(wl.tree)
+
+    class W:  # the flattened batch with the workload's shape
+        pass
+
+    fw = W()
+    fw.__dict__.update(wl.__dict__)
+    fw.batch = batch
+    fw.num_queries = len(batch["query_group"])
+    plan = P.psa_build_plan(_cfg(wl), batch)
+    kinds = plan.items()[::4, 0] & 0xFF
+    for x in range(8):
+        local = kinds[x::8]
+        pos = np.nonzero(local == 2)[0]
+        n, npx = len(local), len(pos)
+        assert npx == 128 and pos[0] == 0
+        gaps = np.diff(pos)
+        assert gaps.max() <= -(-n // npx) and gaps.min() >= n // npx - 1
+    _check_coverage(fw, plan)
+    kinds = P.psa_build_plan(_cfg(wl), batch, flags=P.NO_TILE_PAIRS).items()[::4, 0] & 0xFF
+    for x in range(8):
+        assert list(np.nonzero(kinds[x::8] == 2)[0]) == list(range(128))
+
+
 def test_peak_entry_points_reject_bad_arguments():
     """Argument checks of psa_debug_read_peak / psa_debug_mfma_peak come before
     any device access (no GPU needed): NULL pointers, sizes out of range, and
