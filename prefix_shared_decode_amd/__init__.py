@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     FORCE_MATVEC,
     LIB_PATH,
     NO_TILE_PAIRS,
+    NO_PAGE_SHARING,
     NO_XCD_ORDER,
     PREFIX_ONLY,
     PSA_BF16,

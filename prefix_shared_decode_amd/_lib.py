@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libpsa.so")
 
 PSA_BF16, PSA_F32 = 0, 1
 PREFIX_ONLY, DISTINCT_ONLY, FORCE_MATVEC, DEBUG_POISON, NO_XCD_ORDER, NO_TILE_PAIRS = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
+NO_PAGE_SHARING = 0x40
 STATUS = {0: "PSA_OK", 1: "PSA_ERR_INVALID_ARGUMENT", 2: "PSA_ERR_UNSUPPORTED", 3: "PSA_ERR_OUT_OF_RANGE",
           4: "PSA_ERR_WORKSPACE_TOO_SMALL", 5: "PSA_ERR_HIP", 6: "PSA_ERR_ALLOC"}
 

@@ -69,7 +69,8 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   psa_plan_opts o{};
   if (opts_in) o = *opts_in;
   const uint32_t known = PSA_PLAN_PREFIX_ONLY | PSA_PLAN_DISTINCT_ONLY | PSA_PLAN_FORCE_MATVEC |
-                         PSA_PLAN_DEBUG_POISON | PSA_PLAN_NO_XCD_ORDER | PSA_PLAN_NO_TILE_PAIRS;
+                         PSA_PLAN_DEBUG_POISON | PSA_PLAN_NO_XCD_ORDER | PSA_PLAN_NO_TILE_PAIRS |
+                         PSA_PLAN_NO_PAGE_SHARING;
   if (o.flags & ~known) return set_error(PSA_ERR_INVALID_ARGUMENT, "unknown plan flag");
   if ((o.flags & PSA_PLAN_PREFIX_ONLY) && (o.flags & PSA_PLAN_DISTINCT_ONLY))
     return set_error(PSA_ERR_INVALID_ARGUMENT, "PREFIX_ONLY and DISTINCT_ONLY are exclusive");
@@ -153,13 +154,68 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     group_mfma[g] = bf16 && !(o.flags & PSA_PLAN_FORCE_MATVEC) && rows >= o.mfma_min_rows;
     if (!group_mfma[g]) group_chunk[g] = std::min<int64_t>(Cp, kMaxMatvecPages * 16);
   }
-  // partial counts per query: prefix chunks first, then distinct chunks
+  // Families: runs of consecutively numbered groups whose prefixes begin
+  // with the same pages, as a flattened multi-level tree produces for the
+  // sub-groups of one root (BatchLLM summary §4.2: flattening gives each
+  // group its own copy of the shared root).  The tokens [0, S) that a family
+  // shares are covered once, by MFMA tiles whose rows span every member of
+  // the family; each group's own part [S, Lp) is tiled as before.  A family
+  // keeps the length its first two groups share; a later group that shares
+  // less ends it.
+  struct Family {
+    int first, last;  // groups first..last
+    int64_t S;        // shared tokens, whole pages
+  };
+  std::vector<Family> fams;
+  std::vector<int32_t> fam_of(G, -1);
+  constexpr int64_t kMinShared = 64;  // at least one 64-token MFMA block
+  if (use_prefix && bf16 && !(o.flags & (PSA_PLAN_FORCE_MATVEC | PSA_PLAN_NO_PAGE_SHARING))) {
+    auto lead = [&](int g, int h) {  // leading whole pages g and h have in common, in tokens
+      const int64_t n = std::min(b->group_prefix_len[g], b->group_prefix_len[h]) / P;
+      const int32_t* pa = b->group_pages + b->group_page_off[g];
+      const int32_t* pb = b->group_pages + b->group_page_off[h];
+      int64_t k = 0;
+      while (k < n && pa[k] == pb[k]) ++k;
+      return k * P;
+    };
+    auto has_members = [&](int g) { return member_off[g + 1] > member_off[g]; };
+    for (int g = 0; g < G;) {
+      int h = g + 1;
+      int64_t S = 0;
+      if (has_members(g)) {
+        for (; h < G && has_members(h); ++h) {
+          const int64_t sh = lead(g, h);
+          if (h == g + 1) {
+            if (sh < kMinShared) break;
+            S = sh;
+          } else if (sh < S) {
+            break;
+          }
+        }
+      }
+      const int64_t rows = (int64_t)(member_off[h] - member_off[g]) * r;
+      if (h - g >= 2 && rows >= o.mfma_min_rows) {
+        for (int t = g; t < h; ++t) fam_of[t] = (int32_t)fams.size();
+        fams.push_back({g, h - 1, S});
+        g = h;
+      } else {
+        ++g;
+      }
+    }
+  }
+  auto shared_len = [&](int g) { return fam_of[g] >= 0 ? fams[fam_of[g]].S : (int64_t)0; };
+  auto shared_chunks = [&](int g) { return fam_of[g] >= 0 ? ceil_div(fams[fam_of[g]].S, Cp) : (int64_t)0; };
+
+  // partial counts per query: prefix chunks first (shared ones, then the
+  // group's own), then distinct chunks
   std::vector<int32_t> n_pc(N, 0), expected(N, 0), slot_off(N, -1);
   int64_t slots = 0;
   for (int i = 0; i < N; ++i) {
     const int g = b->query_group[i];
     const int64_t lp = g >= 0 ? b->group_prefix_len[g] : 0;
-    n_pc[i] = use_prefix && g >= 0 ? (int32_t)ceil_div(lp, group_chunk[g]) : 0;
+    n_pc[i] = use_prefix && g >= 0
+                  ? (int32_t)(shared_chunks(g) + ceil_div(lp - shared_len(g), group_chunk[g]))
+                  : 0;
     const int64_t n_dc = use_distinct ? ceil_div(b->query_distinct_len[i], Cd) : 0;
     expected[i] = n_pc[i] + (int32_t)n_dc;
     if (expected[i] >= 2) {
@@ -186,39 +242,56 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   const double fixed = 300.0;                     // per-item overhead, ns
   int64_t n_prefix_items = 0, n_matvec_items = 0;
   const int64_t tile_max = o.mfma_tile_rows;
-  for (int g = 0; g < G && use_prefix; ++g) {
+  int64_t next_set_id = 0;  // one id per (prefix chunk, kv head): its tiles re-read the same pages
+  // MFMA tiles over rows [row0, row0 + rows) of the member array (a = first
+  // row counted over the whole member array, so a tile finds its queries
+  // without reading a group offset first) for tokens [tb, te) of group g's
+  // pages; j = the chunk's partial index for every query of those rows
+  auto mfma_tiles = [&](int g, int64_t row0, int64_t rows, int32_t tb, int32_t te, int64_t j) {
+    const int32_t pbase = (int32_t)(b->group_page_off[g] + tb / P);
+    const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
+    const int64_t ntiles = ceil_div(rows, tile_max);
+    const int64_t per = round_up(ceil_div(rows, ntiles), 16);
+    for (int kvh = 0; kvh < hkv; ++kvh) {
+      const int64_t set = next_set_id++;
+      for (int64_t rb = 0; rb < rows; rb += per) {
+        const int64_t rc = std::min(per, rows - rb);
+        WorkItem it{(int32_t)(ITEM_PREFIX_MFMA | (j << 8)), kvh, g, tb, te, pbase, (int32_t)(row0 + rb), (int32_t)rc};
+        const double fl = (double)round_up(te - tb, 64) * round_up(rc, 16) * d * 4;
+        mfma.push_back({it, fixed + std::max(fl / mfma_slot, 4.0 * kv_bytes / bw_wave)});
+        mfma_set.push_back(set);
+        ++n_prefix_items;
+      }
+    }
+  };
+  for (size_t f = 0; f < fams.size() && use_prefix; ++f) {  // the families' shared tokens
+    const Family& F = fams[f];
+    const int64_t rows = (int64_t)(member_off[F.last + 1] - member_off[F.first]) * r;
+    for (int64_t ch = 0; ch < ceil_div(F.S, Cp); ++ch)
+      mfma_tiles(F.first, (int64_t)member_off[F.first] * r, rows, (int32_t)(ch * Cp),
+                 (int32_t)std::min(F.S, (ch + 1) * Cp), ch);
+  }
+  for (int g = 0; g < G && use_prefix; ++g) {  // each group's own tokens
     const int64_t lp = b->group_prefix_len[g];
     const int nm = member_off[g + 1] - member_off[g];
-    if (lp == 0 || nm == 0) continue;
+    const int64_t S = shared_len(g), j0 = shared_chunks(g);
+    if (lp == S || nm == 0) continue;
     const int64_t rows = (int64_t)nm * r;
     const bool mf = group_mfma[g];
     const int64_t C = group_chunk[g];
-    const int64_t nchunks = ceil_div(lp, C);
+    const int64_t nchunks = ceil_div(lp - S, C);
     for (int64_t ch = 0; ch < nchunks; ++ch) {
-      const int32_t tb = (int32_t)(ch * C), te = (int32_t)std::min(lp, (ch + 1) * C);
-      const int32_t pbase = (int32_t)(b->group_page_off[g] + tb / P);
-      const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
+      const int32_t tb = (int32_t)(S + ch * C), te = (int32_t)std::min(lp, S + (ch + 1) * C);
+      const int64_t j = j0 + ch;
       if (mf) {
-        const int64_t ntiles = ceil_div(rows, tile_max);
-        const int64_t per = round_up(ceil_div(rows, ntiles), 16);
-        for (int kvh = 0; kvh < hkv; ++kvh) {
-          for (int64_t rb = 0; rb < rows; rb += per) {
-            const int64_t rc = std::min(per, rows - rb);
-            // a = first row counted over the whole member array, so the tile finds
-            // its queries without reading the group's member offset first
-            WorkItem it{(int32_t)(ITEM_PREFIX_MFMA | (ch << 8)), kvh, g, tb, te, pbase,
-                        (int32_t)(member_off[g] * r + rb), (int32_t)rc};
-            const double fl = (double)round_up(te - tb, 64) * round_up(rc, 16) * d * 4;
-            mfma.push_back({it, fixed + std::max(fl / mfma_slot, 4.0 * kv_bytes / bw_wave)});
-            mfma_set.push_back(((int64_t)g * nchunks + ch) * hkv + kvh);
-            ++n_prefix_items;
-          }
-        }
+        mfma_tiles(g, (int64_t)member_off[g] * r, rows, tb, te, j);
       } else {
+        const int32_t pbase = (int32_t)(b->group_page_off[g] + tb / P);
+        const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
         for (int t = member_off[g]; t < member_off[g + 1]; ++t) {
           const int qi = members[t];
           for (int kvh = 0; kvh < hkv; ++kvh) {
-            const int32_t slot = expected[qi] >= 2 ? (int32_t)(((int64_t)slot_off[qi] + ch) * hkv + kvh) : -1;
+            const int32_t slot = expected[qi] >= 2 ? (int32_t)(((int64_t)slot_off[qi] + j) * hkv + kvh) : -1;
             WorkItem it{ITEM_MATVEC, kvh, qi, tb, te, pbase, expected[qi], slot};
             waves.push_back({it, fixed + kv_bytes / bw_wave});
             ++n_matvec_items;
@@ -310,8 +383,23 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
       for (int64_t t = s.begin; t < s.end; ++t) q[best].push_back(order[t]);
       load[best] += s.cost;
     }
-    for (auto& qq : q)
-      std::stable_sort(qq.begin(), qq.end(), [&](int64_t a, int64_t b2) { return units[a].cost > units[b2].cost; });
+    // Longest first.  A queue of MFMA tiles alone (a PREFIX_ONLY plan) puts
+    // family tiles first instead: they pair with the groups' own, longer
+    // tiles on the CUs (flattened 4x16x16 prefix-only: 0.126 ms against
+    // 0.140 ms longest first).
+    auto family = [&](int64_t u) {
+      const WorkItem& w = units[u].it[0];
+      return w.kind % 256 == ITEM_PREFIX_MFMA && (int64_t)w.a + w.b > (int64_t)member_off[w.id + 1] * r;
+    };
+    for (auto& qq : q) {
+      const bool tiles_only = std::all_of(qq.begin(), qq.end(), [&](int64_t u) {
+        return units[u].it[0].kind % 256 == ITEM_PREFIX_MFMA;
+      });
+      std::stable_sort(qq.begin(), qq.end(), [&](int64_t a, int64_t b2) {
+        if (tiles_only && family(a) != family(b2)) return family(a);
+        return units[a].cost > units[b2].cost;
+      });
+    }
     // Tile pairs: when the launch starts, an XCD's units k and k + 32 land on
     // the same compute unit (its 32 CUs are filled in one fixed order, twice:
     // two workgroups fit per CU).  Placing an XCD's first MFMA tiles at
@@ -324,14 +412,14 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
         size_t np = 0;
         while (np < qq.size() && units[qq[np]].it[0].kind % 256 == ITEM_PREFIX_MFMA) ++np;
         if (np > 2 * (size_t)kCusPerXcd && qq.size() > np) {
-          // More tiles than one round of pairs: spread them evenly through
-          // the queue, so that MFMA tiles (latency bound) and mat-vec units
-          // (HBM bound) run side by side instead of one phase after the
-          // other.  (Measured on the two-level 4x16x16 shape: 0.262 ms
-          // against 0.270 ms with the tiles first; spreading them over the
-          // first 70% only gave 0.266 ms.)
+          // More tiles than one round of pairs: spread them evenly over the
+          // first 3/4 of the queue, so that MFMA tiles (latency bound) and
+          // mat-vec units (HBM bound) run side by side instead of one phase
+          // after the other, and short mat-vec units end the launch.
+          // (Flattened 4x16x16 with family tiles: 0.254 ms; tiles first
+          // 0.270, spread over the whole queue 0.270.)
           const size_t n = qq.size();
-          const size_t span = n;
+          const size_t span = std::max(np, (size_t)(0.75 * (double)n));
           std::vector<int64_t> re;
           re.reserve(n);
           size_t mv = np, tk = 0;

@@ -109,6 +109,21 @@ def test_library_loaded_before_torch_initialises_the_gpu():
     assert err <= 1e-2, r.stdout
 
 
+@pytest.mark.parametrize("r,d", [(1, 128), (4, 64), (4, 128), (8, 128)])
+@pytest.mark.parametrize("opts", [dict(), dict(prefix_chunk_tokens=32, mfma_tile_rows=16),
+                                  dict(flags=P.NO_PAGE_SHARING), dict(mfma_min_rows=1)],
+                         ids=["default", "small_chunks", "no_sharing", "min_rows_1"])
+def test_family_tiles(r, d, opts):
+    """Consecutive groups that begin with the same pages: one set of MFMA
+    tiles over all their members covers those pages, next to empty and
+    mat-vec sized rests of each group."""
+    from workloads import build_family_case
+
+    wl = build_family_case(7, r=r, d=d)
+    q, k, v = values(wl)
+    _check_full(wl, wl.batch, q, k, v, f"family r{r} d{d} {opts}", **opts)
+
+
 # ---------------- edge cases ----------------
 
 def test_stale_padding_is_masked():

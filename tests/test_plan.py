@@ -61,6 +61,7 @@ def _coverage(wl, plan):
     for i, g in enumerate(b["query_group"]):
         if g >= 0:
             members.setdefault(int(g), []).append(i)
+    member_list = [i for g in sorted(members) for i in members[g]]  # the plan's member array
     items = plan.items()
     assert len(items) % 4 == 0
     for u in range(len(items) // 4):
@@ -84,9 +85,18 @@ def _coverage(wl, plan):
             assert a % r == 0 and bb % r == 0 and 0 < bb <= 128
             assert pbase == b["group_page_off"][ident] + tb // 16
             first = sum(len(members.get(g2, [])) for g2 in range(ident))  # the group's first member, over all groups
-            assert first * r <= a and a + bb <= (first + len(members[ident])) * r
+            assert first * r <= a
+            # rows past the group's own members belong to the following groups,
+            # which must hold the same pages for these tokens (a family tile)
+            own = b["group_pages"][b["group_page_off"][ident] + tb // 16: b["group_page_off"][ident] + (te + 15) // 16]
             for mi in range(a // r, (a + bb) // r):
-                cov.setdefault((members[ident][mi - first], kvh), []).append(("p", tb, te, kind_full >> 8, None))
+                qi = member_list[mi]
+                g2 = int(b["query_group"][qi])
+                if g2 != ident:
+                    assert g2 > ident and te <= b["group_prefix_len"][g2]
+                    other = b["group_pages"][b["group_page_off"][g2] + tb // 16: b["group_page_off"][g2] + (te + 15) // 16]
+                    assert list(other) == list(own), (ident, g2, tb, te)
+                cov.setdefault((qi, kvh), []).append(("p", tb, te, kind_full >> 8, None))
         elif kind == 3:
             for kvh2 in range(wl.num_kv_heads):
                 cov.setdefault((ident, kvh2), []).append(("e", 0, 0, 0, None))
@@ -374,10 +384,12 @@ def test_mfma_tiles_start_two_to_a_cu():
 
 
 def test_mfma_tiles_spread_when_more_than_a_round_of_pairs():
-    """The flattened two-level shape has 128 MFMA tiles per XCD queue (more
-    than two per CU): they are spread evenly through each queue, interleaved
-    with the mat-vec units, instead of leading it; NO_TILE_PAIRS keeps them
-    first.  Both orders cover every (query, kv head) exactly."""
+    """The flattened two-level shape without family tiles has 128 MFMA tiles
+    per XCD queue (more than two per CU): they are spread evenly over the
+    first three quarters of each queue, interleaved with the mat-vec units,
+    instead of leading it;
+    NO_TILE_PAIRS keeps them first.  Both orders cover every (query, kv head)
+    exactly."""
     from workloads import make_workload
 
     wl = make_workload("two_level_4x16x16")
@@ -390,7 +402,7 @@ def test_mfma_tiles_spread_when_more_than_a_round_of_pairs():
     fw.__dict__.update(wl.__dict__)
     fw.batch = batch
     fw.num_queries = len(batch["query_group"])
-    plan = P.psa_build_plan(_cfg(wl), batch)
+    plan = P.psa_build_plan(_cfg(wl), batch, flags=P.NO_PAGE_SHARING)
     kinds = plan.items()[::4, 0] & 0xFF
     for x in range(8):
         local = kinds[x::8]
@@ -398,11 +410,75 @@ def test_mfma_tiles_spread_when_more_than_a_round_of_pairs():
         n, npx = len(local), len(pos)
         assert npx == 128 and pos[0] == 0
         gaps = np.diff(pos)
-        assert gaps.max() <= -(-n // npx) and gaps.min() >= n // npx - 1
+        span = int(0.75 * n)  # spread over the first three quarters of the queue
+        assert gaps.max() <= -(-span // npx) and gaps.min() >= span // npx - 1 and pos[-1] < span
     _check_coverage(fw, plan)
-    kinds = P.psa_build_plan(_cfg(wl), batch, flags=P.NO_TILE_PAIRS).items()[::4, 0] & 0xFF
+    kinds = P.psa_build_plan(_cfg(wl), batch, flags=P.NO_TILE_PAIRS | P.NO_PAGE_SHARING).items()[::4, 0] & 0xFF
     for x in range(8):
         assert list(np.nonzero(kinds[x::8] == 2)[0]) == list(range(128))
+
+
+def _flat(wl):
+    batch, _ = P.psa_flatten_prefix_tree(wl.tree)
+
+    class W:  # the flattened batch with the workload's shape
+        pass
+
+    fw = W()
+    fw.__dict__.update(wl.__dict__)
+    fw.batch = batch
+    fw.num_queries = len(batch["query_group"])
+    return fw
+
+
+def test_family_tiles_cover_a_shared_root_once():
+    """Flattened 4x16x16: the 16 groups of a root begin with the root's 64
+    pages, so its 1024 tokens are tiled once over all 256 members (8 tiles of
+    128 rows per kv head), and each group keeps one 2048-token chunk of its
+    own: 4*8*8 + 64*8 = 768 MFMA tiles, 3 pieces per query as before."""
+    from workloads import make_workload
+
+    fw = _flat(make_workload("two_level_4x16x16"))
+    b = fw.batch
+    plan = P.psa_build_plan(_cfg(fw), b)
+    it = plan.items()
+    mf = it[(it[:, 0] & 0xFF) == 2]
+    assert len(mf) == 768 and plan.info()["num_prefix_items"] == 768
+    fam = mf[mf[:, 4] == 1024]
+    assert len(fam) == 256 and (fam[:, 3] == 0).all() and (fam[:, 7] == 128).all()
+    assert ((fam[:, 0] >> 8) == 0).all()
+    own = mf[mf[:, 3] == 1024]
+    assert len(own) == 512 and (own[:, 4] == 3072).all() and ((own[:, 0] >> 8) == 1).all()
+    expected, _ = plan.queries()
+    assert (expected == 3).all()
+    _check_coverage(fw, plan)
+    plain = P.psa_build_plan(_cfg(fw), b, flags=P.NO_PAGE_SHARING)
+    assert plain.info()["num_prefix_items"] == 1024
+    _check_coverage(fw, plain)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("r", [1, 4, 8])
+def test_family_tiles_edge_shapes(seed, r):
+    """Family tiles next to empty and mat-vec own parts, several chunks of the
+    shared part, small tiles, and the PREFIX_ONLY / DISTINCT_ONLY plans: every
+    token is covered once and the partial counts match."""
+    from workloads import build_family_case
+
+    wl = build_family_case(seed, r=r)
+    plan = P.psa_build_plan(_cfg(wl), wl.batch)
+    it = plan.items()
+    mf = it[(it[:, 0] & 0xFF) == 2]
+    rows = (3 + 2 + 1 + 1) * r  # the family's members
+    fam = mf[(mf[:, 2] == 0) & (mf[:, 4] <= 64)]
+    if rows >= 16:
+        assert len(fam) > 0 and fam[fam[:, 1] == 0][:, 7].sum() == rows
+    for kw in ({}, {"prefix_chunk_tokens": 32}, {"prefix_chunk_tokens": 48, "mfma_tile_rows": 16},
+               {"flags": P.PREFIX_ONLY}, {"flags": P.DISTINCT_ONLY}, {"flags": P.NO_PAGE_SHARING},
+               {"mfma_min_rows": 1}):
+        plan = P.psa_build_plan(_cfg(wl), wl.batch, **kw)
+        fl = kw.get("flags", 0)
+        _check_coverage(wl, plan, prefix=not fl & P.DISTINCT_ONLY, distinct=not fl & P.PREFIX_ONLY)
 
 
 def test_peak_entry_points_reject_bad_arguments():

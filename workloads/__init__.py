@@ -10,6 +10,8 @@ from .synth import (  # noqa: F401
     make_workload,
     build_single_level,
     build_two_level,
+    share_leading_pages,
+    build_family_case,
     make_values,
     fill_stale,
     algorithmic_cost,

@@ -102,6 +102,31 @@ def build_single_level(name, hq, hkv, d, dtype, groups, ungrouped_lens, seed=0,
     return Workload(name, hq, hkv, d, dtype, num_pages, batch, None, seed, P)
 
 
+def share_leading_pages(wl, first, last, pages):
+    """Make groups first+1..last begin with the first `pages` page ids of
+    group `first` (in place): the shape a flattened tree gives the groups
+    below one shared node.  Their own pages there become unused."""
+    b = wl.batch
+    off, gp = b["group_page_off"], b["group_pages"]
+    for g in range(first + 1, last + 1):
+        n = min(pages, int(off[g + 1] - off[g]), int(off[first + 1] - off[first]))
+        gp[off[g]: off[g] + n] = gp[off[first]: off[first] + n]
+    return wl
+
+
+def build_family_case(seed, r=4, hkv=2, d=64):
+    """Groups 0..3 begin with the same 4 pages (64 tokens): group 1's prefix
+    is exactly those pages, group 0 has a ragged rest, groups 2 and 3 have
+    one request each; group 4 shares nothing with them and group 5 shares 3
+    pages with group 4.  Plus two requests without a group."""
+    wl = build_single_level("family_case", hkv * r, hkv, d, "bf16",
+                            [(100, 3, (0, 30)), (64, 2, (1, 20)), (200, 1, (0, 50)), (70, 1, (1, 9)),
+                             (90, 5, (0, 40)), (48, 4, (1, 30))], (2, (1, 60)), seed=seed)
+    share_leading_pages(wl, 0, 3, 4)
+    share_leading_pages(wl, 4, 5, 3)
+    return wl
+
+
 def build_two_level(name, hq, hkv, d, dtype, n_roots, root_len, n_subs, sub_len,
                     n_req, dist_range, seed=0, P=PAGE):
     """Two-level prefix tree: roots -> sub-prefixes -> requests.
