@@ -91,7 +91,7 @@ def cpu_baseline(wl, batch, q, k, v, target_s, max_s):
     rng = np.random.default_rng(123)
     order = rng.permutation(n)
 
-    def run(count):
+    def run(count, passes=1):
         import torch
 
         qs = sorted(int(x) for x in order[:count])
@@ -101,7 +101,8 @@ def cpu_baseline(wl, batch, q, k, v, target_s, max_s):
         vs = v.index_select(0, idx).float().cpu().numpy()
         qh = q.index_select(0, torch.as_tensor(qs, device=q.device)).float().cpu().numpy()
         t0 = time.perf_counter()
-        oracle.decode_attention(qh, ks, vs, sub)
+        for _ in range(passes):
+            oracle.decode_attention(qh, ks, vs, sub)
         return time.perf_counter() - t0
 
     count = 4
@@ -115,13 +116,18 @@ def cpu_baseline(wl, batch, q, k, v, target_s, max_s):
     while el > max_s and count > 1:
         count = max(1, count // 2)
         el = run(count)
+    passes = 1
+    if count == n and el < target_s / 2:  # the whole workload is quick: time several passes over it
+        passes = min(8, max(1, int(target_s / max(el, 1e-3))))
+        el = run(count, passes)
     return {
-        "value": count / el,
+        "value": count * passes / el,
         "unit": "queries/s",
         "cores": int(threads),
         "host_cpus": os.cpu_count(),
         "kind": "oracle",
-        "sample": f"{count} of {n} queries of {wl.name} (all heads), fp64 numpy oracle, {el:.1f} s",
+        "sample": f"{count} of {n} queries of {wl.name} (all heads), {passes} pass(es), fp64 numpy oracle, "
+                  f"{el:.1f} s",
         "note": "plain fp64 oracle on the host cores: a reported baseline, not the target",
     }
 
