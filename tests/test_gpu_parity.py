@@ -124,6 +124,34 @@ def test_family_tiles(r, d, opts):
     _check_full(wl, wl.batch, q, k, v, f"family r{r} d{d} {opts}", **opts)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_small_workloads(seed):
+    """Seeded random shapes: GQA ratio, head dim, group sizes and prefix
+    lengths (ragged, some groups sharing their leading pages), distinct
+    lengths including empty ones, and random chunk / tile options."""
+    from workloads import share_leading_pages
+
+    rng = np.random.default_rng(100 + seed)
+    r = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4])) if r > 1 else int(rng.choice([2, 8]))
+    d = int(rng.choice([64, 128]))
+    groups = []
+    for _ in range(int(rng.integers(1, 6))):
+        n = int(rng.integers(1, 30))
+        groups.append((int(rng.integers(1, 700)), n, (0, int(rng.integers(1, 400)))))
+    wl = build_single_level(f"rand{seed}", hkv * r, hkv, d, "bf16", groups, (int(rng.integers(0, 5)), (1, 500)),
+                            seed=seed, spare_pages=3)
+    if len(groups) >= 2 and rng.random() < 0.7:  # the first groups begin with the same pages
+        share_leading_pages(wl, 0, int(rng.integers(1, len(groups))), int(rng.integers(1, 20)))
+    opts = {}
+    if rng.random() < 0.5:
+        opts = dict(prefix_chunk_tokens=int(rng.choice([64, 256, 1024, 2048])),
+                    distinct_chunk_tokens=int(rng.choice([32, 128, 1024])),
+                    mfma_tile_rows=int(rng.choice([16, 64, 128])), mfma_min_rows=int(rng.choice([1, 16, 48])))
+    q, k, v = values(wl)
+    _check_full(wl, wl.batch, q, k, v, f"random seed {seed} r{r} hkv{hkv} d{d} {opts}", **opts)
+
+
 # ---------------- edge cases ----------------
 
 def test_stale_padding_is_masked():
