@@ -10,7 +10,8 @@ stream; L2 and the 256 MB MALL are flushed before every step, outside the
 events, by reading a 1 GiB buffer (a read leaves no dirty lines whose
 write-back would be charged to the timed launch).  Prints one JSON line.
 
---gpus N with N > 1 is refused: this build measures one GPU.
+--gpus N with N > 1 is refused: the benchmark measures one GPU; the path
+shards by prefix group or kv head without any exchange between GPUs.
 """
 
 from __future__ import annotations
@@ -316,8 +317,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the prefix-shared decode path shards by prefix group or kv head with no exchange, "
-              "see DESIGN.md", file=sys.stderr)
+              "the prefix-shared decode path shards by prefix group or kv head with no exchange "
+              "between GPUs", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
