@@ -436,6 +436,12 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(wl, batch, q, k, v, args.cpu_seconds, 30.0)
     if args.trace:
         trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, args.trace)
+    rec["context"] = {
+        "note": "figures quoted by the pages; end-to-end serving speedups on other hardware, not measurements "
+                "of this kernel, so no vs_baseline is derived from them",
+        "batchllm_end_to_end_vs_vllm_sglang": "1.3x-10.8x (NVIDIA A100 80GB and AMD MI200)",
+        "feather_scheduler_end_to_end": "2x-10x (NVIDIA RTX 6000 Ada, A100)",
+    }
     line = json.dumps(rec)
     print(line, flush=True)
     if args.json_out:
