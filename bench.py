@@ -294,7 +294,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama3_8b_8x100")
+    ap.add_argument("--workload", default="llama3_8b_8x100",
+                    help="a preset of workloads/synth.py, or 'all': one JSON line per preset")
     ap.add_argument("--no-flush", action="store_true", help="do not flush L2/MALL between steps")
     ap.add_argument("--write-flush", action="store_true",
                     help="flush by writing 1 GiB (leaves dirty lines) instead of reading it")
@@ -321,6 +322,18 @@ def main():
               "between GPUs", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "all":
+        from workloads import PRESETS
+
+        for name in PRESETS:
+            args.workload = name
+            run_one(args)
+        return
+    run_one(args)
+
+
+def run_one(args):
+    """Time one workload and print its JSON line."""
     import numpy as np
     import torch
 
