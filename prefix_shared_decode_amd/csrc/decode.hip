@@ -660,30 +660,36 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
 constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
-// Copy 16 bytes per lane from gbase + voff to LDS at lds + 16 * lane through
-// the load unit (global_load_lds_dwordx4, saddr form; M0 holds the LDS base
-// and is restored).  Written as inline asm so that the compiler does not make
-// every later LDS read wait for these copies: completion is awaited
-// explicitly with s_waitcnt vmcnt, followed by a barrier.  The LDS pointer is
-// an operand so that the compiler knows the stage may change.
-__device__ __forceinline__ void copy_to_lds(const char* gbase, uint32_t voff, lds_char* lds) {
-  // both bases are wave-uniform; say so, so that they are in scalar registers
-  // whatever the register allocator did with the arithmetic that made them
-  // (readfirstlane yields a signed int: widen each half as unsigned)
-  const uint64_t gb = reinterpret_cast<uint64_t>(gbase);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gb);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(gb >> 32));
-  gbase = reinterpret_cast<const char*>(((uint64_t)hi << 32) | (uint64_t)lo);
-  lds = (lds_char*)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+// A wave-uniform 64-bit address in scalar registers, whatever the register
+// allocator did with the arithmetic that made it (readfirstlane yields a
+// signed int: each half is widened as unsigned).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t a) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+// Copy 16 bytes per lane from kbase + voff to LDS at lds_k + 16 * lane and
+// from vbase + voff to lds_v + 16 * lane, through the load unit
+// (global_load_lds_dwordx4, saddr form; M0 holds the LDS destination and is
+// restored: the compiler reserves it).  Written as inline asm so that the
+// compiler does not make every later LDS read wait for these copies:
+// completion is awaited explicitly with s_waitcnt vmcnt, followed by a
+// barrier.  The "memory" clobber tells the compiler that LDS may change.
+__device__ __forceinline__ void copy_kv_to_lds(uint64_t kbase, uint64_t vbase, uint32_t voff, uint32_t lds_k,
+                                               uint32_t lds_v) {
   int saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
+      "global_load_lds_dwordx4 %3, %4\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(gbase)
+      : "s"(lds_k), "s"(lds_v), "v"(voff), "s"(kbase), "s"(vbase)
       : "memory");
 }
 
@@ -893,24 +899,37 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
   const int64_t tile_stride = (int64_t)p.hkv * TILEB;
   // where this wave's copy of block blk comes from: K and V tile bases and
   // the token clamp (tokens past the chunk re-read its last token)
+  // (scalar bases, computed once per block; clamp is false unless this
+  // wave's page reaches past the chunk)
   struct Src {
-    const char* ks;
-    const char* vs;
+    uint64_t ks, vs;
     int du, lim;
+    bool clamp;
   };
   auto src = [&](int blk) {
     const int pg = min(blk * 4 + wave, npages - 1);
     const int pid = __builtin_amdgcn_readlane(pid_v, blk);
     const int64_t tile = (int64_t)pid * tile_stride + (int64_t)kvh * TILEB;
     // du > 0 only when this wave's page is past the chunk; lim = last valid token within the page
-    return Src{kp + tile, vp + tile, (blk * 4 + wave - pg) * 16, ntok - 1 - pg * 16};
+    const int du = (blk * 4 + wave - pg) * 16, lim = ntok - 1 - pg * 16;
+    return Src{uniform_u64(reinterpret_cast<uint64_t>(kp + tile)), uniform_u64(reinterpret_cast<uint64_t>(vp + tile)),
+               du, lim, du > 0 || lim < 15};
   };
+  // this lane's source offset of load i in an unclamped page
+  uint32_t off0[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) off0[i] = (uint32_t)(tin[i] * ROW + coff[i]);
   // load i (of NI) of K and of V into a stage; lane l lands at +16 l
+  // (a branch on the uniform clamp flag, not a select: the common path
+  // issues no offset arithmetic)
   auto dma_piece = [&](const Src& c, lds_char* stage, int i) {
-    const uint32_t off = (uint32_t)(min(tin[i] + c.du, c.lim) * ROW + coff[i]);
-    lds_char* dst = stage + (wave * NI + i) * 1024;
-    copy_to_lds(c.ks, off, dst);
-    copy_to_lds(c.vs, off, dst + S::TILE);
+    const uint32_t dst = (uint32_t)(uintptr_t)stage + (uint32_t)((wave * NI + i) * 1024);
+    if (__builtin_expect(c.clamp, 0)) {
+      const uint32_t off = (uint32_t)(min(tin[i] + c.du, c.lim) * ROW + coff[i]);
+      copy_kv_to_lds(c.ks, c.vs, off, dst, dst + S::TILE);
+    } else {
+      copy_kv_to_lds(c.ks, c.vs, off0[i], dst, dst + S::TILE);
+    }
   };
   {
     const Src c = src(0);
