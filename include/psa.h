@@ -219,6 +219,37 @@ psa_status psa_batch_owned_view(const psa_batch_owned* owned, psa_batch* view,
 void psa_free_batch(psa_batch_owned* owned);
 void psa_destroy_plan(psa_plan* plan);
 
+/* Prefix identification from token ids (BatchLLM summary §4.2, and its
+ * prefix-identification step of §5: nested input ids in, prefix-sharing
+ * groups out).  Request i is tokens[token_off[i] .. token_off[i+1]) (host
+ * arrays, borrowed for the call; token_off has num_requests + 1 entries,
+ * starts at 0, non-decreasing).  The requests' compact prefix tree is built
+ * from their lexicographic order and the common prefix lengths of neighbours,
+ * and the dynamic program of psa_flatten_prefix_tree picks the groups that
+ * maximise sum over groups of prefix_len * (members - 1).  A group's members
+ * share their first prefix_len tokens (token-granular: the caller computes
+ * that KV once and each member's distinct part starts at token prefix_len in
+ * pages of its own).  Groups are numbered in the order of their first member.
+ * *out receives a library-owned result (free with psa_free_prefix_groups).
+ * Errors: NULL arrays, offsets not starting at 0 or decreasing
+ * (PSA_ERR_INVALID_ARGUMENT); a request longer than 2^31 tokens
+ * (PSA_ERR_UNSUPPORTED); PSA_ERR_ALLOC. */
+typedef struct psa_prefix_groups psa_prefix_groups;
+psa_status psa_identify_prefix_groups(int32_t num_requests, const int64_t* token_off,
+                                      const int32_t* tokens, psa_prefix_groups** out);
+
+/* View of a result (pointers stay valid until psa_free_prefix_groups; any
+ * output pointer may be NULL): group_prefix_len[num_groups],
+ * group_first_request[num_groups] (a member whose first prefix_len tokens
+ * are the group's prefix), request_group[num_requests] (-1 = no group), and
+ * the saved-token count of the grouping. */
+psa_status psa_prefix_groups_view(const psa_prefix_groups* groups, int32_t* num_groups,
+                                  const int32_t** group_prefix_len,
+                                  const int32_t** group_first_request,
+                                  const int32_t** request_group, int64_t* saved_tokens);
+
+void psa_free_prefix_groups(psa_prefix_groups* groups);
+
 /* Thread-local text of the last non-OK status ("" if none). */
 const char* psa_last_error(void);
 

@@ -14,7 +14,8 @@ Sources (the pages this oracle restates; no listing is copied):
   papercache.org (cited below as *BatchLLM*), §2.2 Eq. 1 (prefix / distinct
   partial attention merged by online softmax), §3.2 Eq. 2 (token-saving
   rate), §4.2 + Fig. 4 (maximising first-level prefix reuse on a compact
-  prefix tree by dynamic programming).
+  prefix tree by dynamic programming), §5 (prefix identification from
+  nested input ids).
 * The continuous-batching post on guijiagi.com (cited as *CB blog*),
   "block management" and "attention computation" sections: paged KV
   blocks, block tables, gather-by-table, truncate to the sequence length,
@@ -40,4 +41,6 @@ from .flatten import (  # noqa: F401
     grouping_saving,
     flatten_tree,
     saving_rate,
+    prefix_tree_from_tokens,
+    identify_groups,
 )

@@ -257,3 +257,76 @@ def saving_rate(logical_tokens, saved_tokens):
     if logical_tokens <= 0:
         return 0.0
     return (1.0 - (logical_tokens - float(saved_tokens)) / logical_tokens) * 100.0
+
+
+def prefix_tree_from_tokens(requests):
+    """Compact prefix tree of token sequences (BatchLLM §4.2: prompts in a
+    compact prefix tree, each node a run of tokens shared by everything below
+    it; the identification step of §5 takes nested input ids).
+
+    Plain construction: a character trie with one node per token position,
+    each trie node counting the requests that pass through it; a trie node
+    is kept as a tree node when at least two requests pass through it and it
+    is the deepest such node before the requests passing through it change
+    (a child with fewer passing requests, or a request ending there).  The
+    kept nodes, linked to their nearest kept ancestor, are the compact tree;
+    a request hangs at the deepest kept node on its path (-1 = none).
+
+    Returns (node_parent, node_len, query_node) in the tree format above.
+    """
+    root = {"kids": {}, "count": 0, "ends": 0, "depth": 0}
+    paths = []
+    for seq in requests:
+        node = root
+        node["count"] += 1
+        path = [node]
+        for t in seq:
+            t = int(t)
+            if t not in node["kids"]:
+                node["kids"][t] = {"kids": {}, "count": 0, "ends": 0, "depth": node["depth"] + 1}
+            node = node["kids"][t]
+            node["count"] += 1
+            path.append(node)
+        node["ends"] += 1
+        paths.append(path)
+
+    def kept(nd):
+        if nd is root or nd["count"] < 2:
+            return False
+        if nd["ends"] > 0:
+            return True
+        return all(c["count"] < nd["count"] for c in nd["kids"].values())
+
+    ids = {}
+    node_parent, node_depth = [], []
+    for path in paths:
+        last = -1
+        for nd in path:
+            if not kept(nd):
+                continue
+            key = id(nd)
+            if key not in ids:
+                ids[key] = len(node_parent)
+                node_parent.append(last)
+                node_depth.append(nd["depth"])
+            last = ids[key]
+    query_node = []
+    for path in paths:
+        q = -1
+        for nd in path:
+            if kept(nd):
+                q = ids[id(nd)]
+        query_node.append(q)
+    node_len = [node_depth[d] - (node_depth[p] if p >= 0 else 0) for d, p in enumerate(node_parent)]
+    return node_parent, node_len, query_node
+
+
+def identify_groups(requests):
+    """Prefix-sharing groups of token sequences: the compact prefix tree,
+    then ``maximize_reuse`` on it.  Returns (saving, group_prefix_len per
+    request, -1 when ungrouped; group node per request)."""
+    node_parent, node_len, query_node = prefix_tree_from_tokens(requests)
+    saving, group_node = maximize_reuse(node_parent, node_len, query_node)
+    a = path_lengths(node_parent, node_len)
+    prefix = [a[g] if g >= 0 else -1 for g in group_node]
+    return saving, prefix, group_node

@@ -2,7 +2,7 @@
 
 The entry points keep the C names (include/psa.h): ``psa_build_plan``,
 ``psa_plan_upload``, ``psa_decode_attention``, ``psa_merge``,
-``psa_flatten_prefix_tree``, ``psa_plan_get_info``.  The library is loaded on
+``psa_flatten_prefix_tree``, ``psa_identify_prefix_groups``, ``psa_plan_get_info``.  The library is loaded on
 first use and its absence is an error.
 """
 
@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     psa_debug_read_peak,
     psa_decode_attention,
     psa_flatten_prefix_tree,
+    psa_identify_prefix_groups,
     psa_merge,
     psa_plan_get_info,
     psa_plan_upload,

@@ -26,7 +26,8 @@ STATUS = {0: "PSA_OK", 1: "PSA_ERR_INVALID_ARGUMENT", 2: "PSA_ERR_UNSUPPORTED", 
 EXPORTS = ["psa_build_plan", "psa_plan_get_info", "psa_plan_upload", "psa_decode_attention", "psa_merge",
            "psa_flatten_prefix_tree", "psa_batch_owned_view", "psa_free_batch", "psa_destroy_plan",
            "psa_last_error", "psa_version", "psa_plan_debug_items", "psa_plan_debug_queries",
-           "psa_decode_attention_traced", "psa_debug_read_peak", "psa_debug_mfma_peak"]
+           "psa_decode_attention_traced", "psa_debug_read_peak", "psa_debug_mfma_peak",
+           "psa_identify_prefix_groups", "psa_prefix_groups_view", "psa_free_prefix_groups"]
 
 
 class PsaError(RuntimeError):
@@ -102,6 +103,11 @@ def lib():
         L.psa_batch_owned_view.argtypes = [vp, C.POINTER(psa_batch), _I64P]
         L.psa_free_batch.argtypes = [vp]
         L.psa_free_batch.restype = None
+        L.psa_identify_prefix_groups.argtypes = [C.c_int32, _I64P, _I32P, C.POINTER(vp)]
+        L.psa_prefix_groups_view.argtypes = [vp, C.POINTER(C.c_int32), C.POINTER(_I32P), C.POINTER(_I32P),
+                                             C.POINTER(_I32P), C.POINTER(C.c_int64)]
+        L.psa_free_prefix_groups.argtypes = [vp]
+        L.psa_free_prefix_groups.restype = None
         L.psa_destroy_plan.argtypes = [vp]
         L.psa_destroy_plan.restype = None
         L.psa_last_error.restype = C.c_char_p
@@ -338,3 +344,30 @@ def psa_flatten_prefix_tree(tree, page_size=16):
         return batch, int(saved.value)
     finally:
         lib().psa_free_batch(h)
+
+
+def psa_identify_prefix_groups(requests):
+    """Prefix-sharing groups of token sequences (include/psa.h): returns a dict
+    with group_prefix_len, group_first_request, request_group (numpy int32)
+    and saved_tokens."""
+    lens = [len(r) for r in requests]
+    off = np.zeros(len(requests) + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lens) if lens else []
+    toks = np.concatenate([np.asarray(r, dtype=np.int32) for r in requests]) if sum(lens) else np.zeros(1, np.int32)
+    toks = np.ascontiguousarray(toks, dtype=np.int32)
+    h = C.c_void_p()
+    _check(lib().psa_identify_prefix_groups(len(requests), off.ctypes.data_as(_I64P), toks.ctypes.data_as(_I32P),
+                                            C.byref(h)))
+    try:
+        ng = C.c_int32()
+        gl, gf, rg = _I32P(), _I32P(), _I32P()
+        saved = C.c_int64()
+        _check(lib().psa_prefix_groups_view(h, C.byref(ng), C.byref(gl), C.byref(gf), C.byref(rg), C.byref(saved)))
+
+        def grab(ptr, n):
+            return np.ctypeslib.as_array(ptr, shape=(n,)).astype(np.int32, copy=True) if n else np.zeros(0, np.int32)
+
+        return {"group_prefix_len": grab(gl, ng.value), "group_first_request": grab(gf, ng.value),
+                "request_group": grab(rg, len(requests)), "saved_tokens": int(saved.value)}
+    finally:
+        lib().psa_free_prefix_groups(h)

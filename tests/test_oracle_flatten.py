@@ -7,6 +7,10 @@
 * Closed form: the two-level 4 x 16 x 16 workload saves 64 * 3072 * 15
   tokens when every sub-prefix forms its own group.
 * Flattening keeps every query's token sequence.
+* Token-level identification (compact tree from token ids + the DP): the
+  Fig. 4 reading written as token sequences gives the golden tree and its
+  savings; on tiny random token sets the result equals the best partition
+  of the requests with each group saving LCP(group) * (size - 1).
 """
 
 import json
@@ -172,3 +176,88 @@ def test_dp_pin_catches_planted_mistake(monkeypatch):
     monkeypatch.setattr(oracle, "grouping_saving", bad)
     with pytest.raises(AssertionError):
         test_fig4_printed_savings()
+
+
+# ---------------- prefix identification from token ids ----------------
+
+FIG4_TOKENS = [[1, 50], [2, 60, 61], [2, 70], [2, 3, 4, 5, 6, 7, 8, 9, 80], [2, 3, 4, 5, 6, 7, 8, 9, 90, 91], [2, 99]]
+
+
+def test_tokens_fig4_reading():
+    """Prompt 1 starts with 'a', prompts 2-6 with 'b'; prompts 4 and 5 share
+    8 tokens.  The tree keeps the nodes shared by two or more prompts: 'b'
+    (depth 1) and the 8-token run (depth 8, under 'b')."""
+    with open(os.path.join(GOLDEN, "fig4_reuse.json")) as f:
+        g = json.load(f)
+    parent, length, qnode = oracle.prefix_tree_from_tokens(FIG4_TOKENS)
+    assert parent == [-1, 0] and length == [1, 7] and qnode == [-1, 0, 0, 1, 1, 0]
+    printed = {p["saving"] for p in g["printed"]}
+    assert F.grouping_saving(parent, length, qnode, [-1, 0, 0, 0, 0, 0]) in printed  # all five under 'b'
+    assert F.grouping_saving(parent, length, qnode, [-1, -1, -1, 1, 1, -1]) in printed  # prompts 4 and 5
+    saving, prefix, _ = oracle.identify_groups(FIG4_TOKENS)
+    assert saving == g["derived_optimum"]["saving"] and prefix == [-1, 1, 1, 8, 8, 1]
+
+
+def lcp(a, b):
+    k = 0
+    while k < min(len(a), len(b)) and a[k] == b[k]:
+        k += 1
+    return k
+
+
+def brute_force_tokens(seqs):
+    best = 0
+    for part in set_partitions(list(range(len(seqs)))):
+        tot = 0
+        for grp in part:
+            if len(grp) >= 2:
+                common = min(lcp(seqs[grp[0]], seqs[j]) for j in grp[1:])
+                tot += common * (len(grp) - 1)
+        best = max(best, tot)
+    return best
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_tokens_identification_matches_brute_force(seed):
+    rng = np.random.default_rng(500 + seed)
+    n = int(rng.integers(1, 8))
+    alphabet = int(rng.integers(1, 4))
+    seqs = [list(rng.integers(0, alphabet, size=int(rng.integers(0, 7)))) for _ in range(n)]
+    if rng.random() < 0.3 and n >= 2:  # duplicates and prefixes of other requests
+        seqs[1] = list(seqs[0])
+        if n >= 3:
+            seqs[2] = list(seqs[0][: len(seqs[0]) // 2])
+    saving, prefix, _ = oracle.identify_groups(seqs)
+    assert saving == brute_force_tokens(seqs)
+    # the grouping itself is valid and worth what it claims
+    groups = {}
+    for i, p in enumerate(prefix):
+        if p >= 0:
+            groups.setdefault(p, []).append(i)
+    claimed = 0
+    _, _, gnode = oracle.identify_groups(seqs)
+    by_node = {}
+    for i, gn in enumerate(gnode):
+        if gn >= 0:
+            by_node.setdefault(gn, []).append(i)
+    for members in by_node.values():
+        p = prefix[members[0]]
+        assert len(members) >= 2 and all(prefix[j] == p for j in members)
+        assert all(len(seqs[j]) >= p and list(seqs[j][:p]) == list(seqs[members[0]][:p]) for j in members)
+        claimed += p * (len(members) - 1)
+    assert claimed == saving
+
+
+def test_tokens_tree_pin_catches_planted_mistake(monkeypatch):
+    """Keeping a node where all requests continue together (no branch)
+    would split a run; the Fig. 4 pin must notice."""
+    orig = F.prefix_tree_from_tokens
+
+    def wrong(requests):
+        parent, length, qnode = orig(requests)
+        return parent, [x + 1 for x in length], qnode  # off by one token per node
+
+    monkeypatch.setattr(F, "prefix_tree_from_tokens", wrong)
+    monkeypatch.setattr(oracle, "prefix_tree_from_tokens", wrong)
+    with pytest.raises(AssertionError):
+        test_tokens_fig4_reading()

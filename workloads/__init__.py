@@ -12,6 +12,7 @@ from .synth import (  # noqa: F401
     build_two_level,
     share_leading_pages,
     build_family_case,
+    build_token_batch,
     make_values,
     fill_stale,
     algorithmic_cost,

@@ -114,6 +114,23 @@ def share_leading_pages(wl, first, last, pages):
     return wl
 
 
+def build_token_batch(n_requests=8000, sharing=3, prefix=(1000, 2100), distinct=(1, 60), system=50, seed=0):
+    """Token-id prompts shaped like the pages' industrial summary workload
+    (about 3 requests per document, documents of about 1570 tokens, a few
+    dozen distinct tokens each), behind a common system prompt: a two-level
+    tree whose best single level is the documents.  Returns a list of int32
+    arrays."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    sys_prompt = rng.integers(0, 32000, size=system, dtype=np.int32)
+    out = []
+    while len(out) < n_requests:
+        doc = rng.integers(0, 32000, size=int(rng.integers(prefix[0], prefix[1] + 1)), dtype=np.int32)
+        for _ in range(min(sharing, n_requests - len(out))):
+            tail = rng.integers(0, 32000, size=int(rng.integers(distinct[0], distinct[1] + 1)), dtype=np.int32)
+            out.append(np.concatenate([sys_prompt, doc, tail]))
+    return out
+
+
 def build_family_case(seed, r=4, hkv=2, d=64):
     """Groups 0..3 begin with the same 4 pages (64 tokens): group 1's prefix
     is exactly those pages, group 0 has a ragged rest, groups 2 and 3 have
