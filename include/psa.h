@@ -85,7 +85,16 @@ typedef struct {
  * group_pages[group_page_off[g] .. group_page_off[g+1]), holding
  * group_prefix_len[g] tokens; likewise per query for its distinct part.
  * query_group[i] = -1: query i shares no prefix.  A query whose context is
- * empty (no prefix and distinct length 0) is rejected. */
+ * empty (no prefix and distinct length 0) is rejected.
+ *
+ * query_prefix_len (may be NULL): query i sees only the first
+ * query_prefix_len[i] tokens of its group's prefix (0 <= value <= the
+ * group's prefix_len; ignored for queries without a group).  This is how a
+ * chunk of prefill tokens shares one launch with decode queries (BatchLLM
+ * §4.3 token batching, Fig. 10c): the chunk is a group whose prefix is the
+ * request's context up to the chunk's end, each chunk token a query that
+ * sees that context up to and including itself (causal), with no distinct
+ * part.  NULL: every query sees its whole group prefix. */
 typedef struct {
   int32_t num_groups;
   const int32_t* group_prefix_len;   /* [num_groups] */
@@ -96,6 +105,7 @@ typedef struct {
   const int32_t* query_distinct_len; /* [num_queries], may be 0 */
   const int64_t* query_page_off;     /* [num_queries + 1] */
   const int32_t* query_pages;        /* [query_page_off[num_queries]] */
+  const int32_t* query_prefix_len;   /* [num_queries] or NULL (see above) */
 } psa_batch;
 
 /* Plan flags. */

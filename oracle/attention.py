@@ -64,13 +64,20 @@ def query_context(batch, i):
 
     BatchLLM §2.2 Eq. 1 / §5: a query of group g sees the group's prefix then
     its own distinct part; a query with no group (``query_group == -1``)
-    sees only its distinct part.
+    sees only its distinct part.  With ``query_prefix_len`` (optional) query
+    i sees only the first ``query_prefix_len[i]`` prefix tokens: a token of a
+    prefill chunk batched with decode queries (BatchLLM §4.3, Fig. 10c)
+    attends causally, to its context up to and including itself.
     """
     segs = []
     g = int(batch["query_group"][i])
     if g >= 0:
         a, b = int(batch["group_page_off"][g]), int(batch["group_page_off"][g + 1])
-        segs.append((batch["group_pages"][a:b], int(batch["group_prefix_len"][g])))
+        lp = int(batch["group_prefix_len"][g])
+        lim = batch.get("query_prefix_len")
+        if lim is not None:
+            lp = min(lp, int(lim[i]))
+        segs.append((batch["group_pages"][a:b], lp))
     a, b = int(batch["query_page_off"][i]), int(batch["query_page_off"][i + 1])
     segs.append((batch["query_pages"][a:b], int(batch["query_distinct_len"][i])))
     return segs

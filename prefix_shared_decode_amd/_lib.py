@@ -51,7 +51,8 @@ _I64P = C.POINTER(C.c_int64)
 class psa_batch(C.Structure):
     _fields_ = [("num_groups", C.c_int32), ("group_prefix_len", _I32P), ("group_page_off", _I64P),
                 ("group_pages", _I32P), ("num_queries", C.c_int32), ("query_group", _I32P),
-                ("query_distinct_len", _I32P), ("query_page_off", _I64P), ("query_pages", _I32P)]
+                ("query_distinct_len", _I32P), ("query_page_off", _I64P), ("query_pages", _I32P),
+                ("query_prefix_len", _I32P)]
 
 
 class psa_plan_opts(C.Structure):
@@ -169,7 +170,9 @@ def _batch_struct(batch, keep):
                      keep(batch["query_group"], np.int32, C.c_int32),
                      keep(batch["query_distinct_len"], np.int32, C.c_int32),
                      keep(batch["query_page_off"] if N else [0], np.int64, C.c_int64),
-                     keep(batch["query_pages"], np.int32, C.c_int32))
+                     keep(batch["query_pages"], np.int32, C.c_int32),
+                     keep(batch["query_prefix_len"], np.int32, C.c_int32)
+                     if batch.get("query_prefix_len") is not None else None)
 
 
 class Plan:

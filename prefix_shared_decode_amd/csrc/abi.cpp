@@ -167,6 +167,7 @@ static psa_status decode_impl(const psa_plan* plan, const void* d_q, const void*
   p.members = reinterpret_cast<const int32_t*>(ws + L.members);
   p.expected = reinterpret_cast<const int32_t*>(ws + L.expected);
   p.slot_off = reinterpret_cast<const int32_t*>(ws + L.slot_off);
+  p.qlim = L.qlim >= 0 ? reinterpret_cast<const int32_t*>(ws + L.qlim) : nullptr;
   p.counters = reinterpret_cast<int32_t*>(ws + L.counters);
   p.part_o = reinterpret_cast<float*>(ws + L.part_o);
   p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
@@ -263,6 +264,7 @@ psa_status psa_batch_owned_view(const psa_batch_owned* o, psa_batch* v, int64_t*
   v->query_distinct_len = o->query_distinct_len.data();
   v->query_page_off = o->query_page_off.data();
   v->query_pages = o->query_pages.data();
+  v->query_prefix_len = nullptr;
   if (saved_tokens) *saved_tokens = o->saved_tokens;
   return PSA_OK;
 }

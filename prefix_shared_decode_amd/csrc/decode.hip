@@ -35,6 +35,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNoMax = -1.0e30f;  // reference max of an empty state (finite: exp2 stays NaN-free)
+constexpr int kNoLimit = 1 << 30;   // MFMA tile: row limit of a query that sees its whole prefix
 constexpr float kLazy = 8.0f;       // MFMA tile: rescale only when a score exceeds the reference max by this
 constexpr float kSlack = 16.0f;     // mat-vec tile: a fixed reference max may be exceeded by this much
 
@@ -716,10 +717,11 @@ struct MfRows {
 };
 
 // One 64-token block (K at Ks, V at Vs) for the wave's NS slices; tokens at or
-// past `valid` are masked.
+// past `valid` are masked, and with `limits` set, tokens at or past the
+// lane's row limit limb[sl] (both counted from the block's first token).
 template <int D, int NS, typename Copy>
 __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, const lds_char* Vs, int valid, float sc,
-                                         const bf16x8& ones, Copy&& copy) {
+                                         const bf16x8& ones, bool limits, const int (&limb)[2], Copy&& copy) {
   constexpr int KK = D / 32, NB = D / 16;
   const int lg = (threadIdx.x & 63) >> 4;
   // ---- S^T tiles: t = kb*2 + half covers tokens 32kb + {8*(m/4) + 4*half + m%4} ----
@@ -753,14 +755,16 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
     copy(t);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (valid < 64) {  // last block of the chunk: mask tokens past its end
+  if (valid < 64 || limits) {  // last block of the chunk, or rows with their own limits
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl)
+    for (int sl = 0; sl < NS; ++sl) {
+      const int lim = min(valid, limb[sl]);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if ((t >> 1) * 32 + 8 * lg + 4 * (t & 1) + i >= valid) s[sl][t][i] = -INFINITY;
+          if ((t >> 1) * 32 + 8 * lg + 4 * (t & 1) + i >= lim) s[sl][t][i] = -INFINITY;
+    }
   }
   // ---- online softmax per row (lane's row = l16; 16 raw scores per lane) ----
   // Each lane checks its own scores against the row's reference max; only
@@ -885,6 +889,20 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     const int row = (wave + kWaves * sl) * 16 + l16;
     qrow[sl] = (sl < ns && row < rc) ? p.members[(rb + row) / R] : -1;
   }
+  // Prefix tokens of this chunk the lane's row sees (a query with a prefix
+  // limit, e.g. a prefill token, sees keys before its own position only);
+  // lmin = the wave's smallest, to find the blocks that need the masks.
+  int lim[2] = {kNoLimit, kNoLimit};
+  int lmin = kNoLimit;
+  if (p.qlim) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+      if (qrow[sl] >= 0) lim[sl] = p.qlim[qrow[sl]] - it.tok_begin;
+    int v = min(lim[0], lim[1]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = min(v, __shfl_xor(v, o));
+    lmin = __builtin_amdgcn_readfirstlane(v);
+  }
 
   // copy of one 64-token block into a stage, global -> LDS through the load
   // unit: this wave's NI loads per tile (index maps in layout.h) all fall in
@@ -989,7 +1007,7 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       const int grow = rb + (wave + kWaves * sl) * 16 + l16;
-      if (qrow[sl] >= 0 && lg == 0 && grow % R == 0 && p.expected[qrow[sl]] > 1)
+      if (qrow[sl] >= 0 && lim[sl] > 0 && lg == 0 && grow % R == 0 && p.expected[qrow[sl]] > 1)
         cval[sl] = __hip_atomic_load(p.counters + (int64_t)qrow[sl] * p.hkv + kvh, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -1010,7 +1028,9 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
         }
       };
       if constexpr (NSL > 0) {
-        mf_block<D, NSL>(st, stage, stage + S::TILE, min(64, ntok - blk * 64), sc, ones, copy);
+        const int limb[2] = {lim[0] - blk * 64, lim[1] - blk * 64};
+        mf_block<D, NSL>(st, stage, stage + S::TILE, min(64, ntok - blk * 64), sc, ones, lmin < blk * 64 + 64, limb,
+                         copy);
       } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t) copy(t);
@@ -1062,7 +1082,7 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
     const float Lr = st.rsum[sl][0];  // every element holds the row's sum
     mt[sl] = max_lane_groups(st.mtrue[sl]);
     const int row = (wave + kWaves * sl) * 16 + l16;
-    valid[sl] = row < rc;
+    valid[sl] = row < rc && lim[sl] > 0;  // (a row whose limit ends before the chunk has no piece here)
     hh[sl] = (rb + row) % R;  // a query's R rows lie in one slice (R divides 16)
     qi[sl] = valid[sl] ? qrow[sl] : 0;
     inv[sl] = 1.f / Lr;  // normalise with the sum of the rounded weights used in P.V

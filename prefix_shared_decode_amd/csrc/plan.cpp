@@ -116,10 +116,24 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     psa_status s = check_segment("query", i, b->query_distinct_len[i], b->query_page_off[i], b->query_page_off[i + 1],
                                  b->query_pages, c.page_size, c.num_pages);
     if (s != PSA_OK) return s;
-    const int64_t lp = g >= 0 ? b->group_prefix_len[g] : 0;
+    int64_t lp = g >= 0 ? b->group_prefix_len[g] : 0;
+    if (b->query_prefix_len && g >= 0) {
+      const int64_t v = b->query_prefix_len[i];
+      if (v < 0 || v > lp)
+        return set_error(PSA_ERR_INVALID_ARGUMENT,
+                         "query " + std::to_string(i) + ": query_prefix_len outside [0, group prefix_len]");
+      lp = v;
+    }
     if (lp + b->query_distinct_len[i] == 0 && !restricted)
       return set_error(PSA_ERR_INVALID_ARGUMENT, "query " + std::to_string(i) + ": empty context");
   }
+  // prefix tokens each query sees (the whole group prefix unless limited)
+  auto visible = [&](int i) -> int64_t {
+    const int g = b->query_group[i];
+    if (g < 0) return 0;
+    return b->query_prefix_len ? (int64_t)b->query_prefix_len[i] : (int64_t)b->group_prefix_len[g];
+  };
+  const bool limited = b->query_prefix_len != nullptr && N > 0;
 
   auto* plan = new (std::nothrow) psa_plan();
   if (!plan) return set_error(PSA_ERR_ALLOC, "out of memory");
@@ -169,7 +183,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   std::vector<Family> fams;
   std::vector<int32_t> fam_of(G, -1);
   constexpr int64_t kMinShared = 64;  // at least one 64-token MFMA block
-  if (use_prefix && bf16 && !(o.flags & (PSA_PLAN_FORCE_MATVEC | PSA_PLAN_NO_PAGE_SHARING))) {
+  if (use_prefix && bf16 && !limited && !(o.flags & (PSA_PLAN_FORCE_MATVEC | PSA_PLAN_NO_PAGE_SHARING))) {
     auto lead = [&](int g, int h) {  // leading whole pages g and h have in common, in tokens
       const int64_t n = std::min(b->group_prefix_len[g], b->group_prefix_len[h]) / P;
       const int32_t* pa = b->group_pages + b->group_page_off[g];
@@ -212,7 +226,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   int64_t slots = 0;
   for (int i = 0; i < N; ++i) {
     const int g = b->query_group[i];
-    const int64_t lp = g >= 0 ? b->group_prefix_len[g] : 0;
+    const int64_t lp = visible(i);  // (families form only without limits: lp is the whole prefix there)
     n_pc[i] = use_prefix && g >= 0
                   ? (int32_t)(shared_chunks(g) + ceil_div(lp - shared_len(g), group_chunk[g]))
                   : 0;
@@ -247,15 +261,23 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   // row counted over the whole member array, so a tile finds its queries
   // without reading a group offset first) for tokens [tb, te) of group g's
   // pages; j = the chunk's partial index for every query of those rows
-  auto mfma_tiles = [&](int g, int64_t row0, int64_t rows, int32_t tb, int32_t te, int64_t j) {
+  auto mfma_tiles = [&](int g, int64_t row0, int64_t rows, int32_t tb, int32_t te_chunk, int64_t j) {
     const int32_t pbase = (int32_t)(b->group_page_off[g] + tb / P);
-    const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
     const int64_t ntiles = ceil_div(rows, tile_max);
     const int64_t per = round_up(ceil_div(rows, ntiles), 16);
     for (int kvh = 0; kvh < hkv; ++kvh) {
       const int64_t set = next_set_id++;
       for (int64_t rb = 0; rb < rows; rb += per) {
         const int64_t rc = std::min(per, rows - rb);
+        int32_t te = te_chunk;
+        if (limited) {  // no tile for rows that all stop before this chunk; none past their last limit
+          int64_t vmax = 0;
+          for (int64_t m = (row0 + rb) / r; m <= (row0 + rb + rc - 1) / r; ++m)
+            vmax = std::max(vmax, visible(members[m]));
+          if (vmax <= tb) continue;
+          te = (int32_t)std::min<int64_t>(te, vmax);
+        }
+        const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
         WorkItem it{(int32_t)(ITEM_PREFIX_MFMA | (j << 8)), kvh, g, tb, te, pbase, (int32_t)(row0 + rb), (int32_t)rc};
         const double fl = (double)round_up(te - tb, 64) * round_up(rc, 16) * d * 4;
         mfma.push_back({it, fixed + std::max(fl / mfma_slot, 4.0 * kv_bytes / bw_wave)});
@@ -272,10 +294,15 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
                  (int32_t)std::min(F.S, (ch + 1) * Cp), ch);
   }
   for (int g = 0; g < G && use_prefix; ++g) {  // each group's own tokens
-    const int64_t lp = b->group_prefix_len[g];
+    int64_t lp = b->group_prefix_len[g];
     const int nm = member_off[g + 1] - member_off[g];
+    if (limited) {  // tokens past every member's limit need no tiles
+      int64_t vmax = 0;
+      for (int t = member_off[g]; t < member_off[g + 1]; ++t) vmax = std::max(vmax, visible(members[t]));
+      lp = vmax;
+    }
     const int64_t S = shared_len(g), j0 = shared_chunks(g);
-    if (lp == S || nm == 0) continue;
+    if (lp <= S || nm == 0) continue;
     const int64_t rows = (int64_t)nm * r;
     const bool mf = group_mfma[g];
     const int64_t C = group_chunk[g];
@@ -290,9 +317,12 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
         const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
         for (int t = member_off[g]; t < member_off[g + 1]; ++t) {
           const int qi = members[t];
+          const int64_t vis = visible(qi);
+          if (vis <= tb) continue;  // this query's prefix ends before the chunk
+          const int32_t tq = (int32_t)std::min<int64_t>(te, vis);
           for (int kvh = 0; kvh < hkv; ++kvh) {
             const int32_t slot = expected[qi] >= 2 ? (int32_t)(((int64_t)slot_off[qi] + j) * hkv + kvh) : -1;
-            WorkItem it{ITEM_MATVEC, kvh, qi, tb, te, pbase, expected[qi], slot};
+            WorkItem it{ITEM_MATVEC, kvh, qi, tb, tq, pbase, expected[qi], slot};
             waves.push_back({it, fixed + kv_bytes / bw_wave});
             ++n_matvec_items;
           }
@@ -471,6 +501,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   L.members = sect((int64_t)members.size() * 4);
   L.expected = sect(N * 4);
   L.slot_off = sect(N * 4);
+  L.qlim = limited ? sect(N * 4) : -1;
   L.counters = sect((int64_t)N * hkv * 4);
   L.meta_bytes = off;
   const int64_t part_o_bytes = slots * hkv * r * d * 4;
@@ -505,6 +536,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   for (int i = 0; i < N; ++i) {
     put32(L.expected, i, expected[i]);
     put32(L.slot_off, i, slot_off[i]);
+    if (limited) put32(L.qlim, i, visible(i));
   }
   // counters stay zero
   plan->num_units = (int64_t)ordered.size();
@@ -521,8 +553,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   for (int g = 0; g < G; ++g)
     if (member_off[g + 1] > member_off[g]) processed += b->group_prefix_len[g];
   for (int i = 0; i < N; ++i) {
-    const int g = b->query_group[i];
-    const int64_t lp = g >= 0 ? b->group_prefix_len[g] : 0;
+    const int64_t lp = visible(i);
     logical += lp + b->query_distinct_len[i];
     prefix_logical += lp;
     processed += b->query_distinct_len[i];

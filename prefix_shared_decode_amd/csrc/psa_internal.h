@@ -38,6 +38,7 @@ constexpr int kMaxPrefixChunk = 2048; // tokens per MFMA prefix chunk (page ids 
 // byte offsets the plan records (int32 everywhere on the device).
 struct ImageLayout {
   int64_t items, pages, member_off, members, expected, slot_off;
+  int64_t qlim;  // visible prefix tokens per query, -1 = no limits (every query sees its whole prefix)
   int64_t counters, part_o, part_ml;
   int64_t meta_bytes;   // bytes copied by the upload (everything before part_o), counters included
   int64_t total_bytes;  // workspace size
@@ -57,6 +58,7 @@ struct DecodeParams {
   const int32_t* members;
   const int32_t* expected;  // partials per query (same for every kv head)
   const int32_t* slot_off;  // first partial slot of each query, -1 if written directly
+  const int32_t* qlim;      // prefix tokens each query sees, or nullptr (all of its group's)
   int32_t* counters;        // [num_queries * hkv] arrivals, self-resetting
   float* part_o;            // [slots * hkv][r][d]
   float* part_ml;           // [slots * hkv][r][2] (m in log2 units, l)

@@ -152,6 +152,22 @@ def test_random_small_workloads(seed):
     _check_full(wl, wl.batch, q, k, v, f"random seed {seed} r{r} hkv{hkv} d{d} {opts}", **opts)
 
 
+@pytest.mark.parametrize("r,d", [(4, 128), (8, 128), (4, 64), (1, 128)])
+@pytest.mark.parametrize("opts", [dict(), dict(prefix_chunk_tokens=64, mfma_tile_rows=32),
+                                  dict(flags=P.FORCE_MATVEC), dict(mfma_min_rows=1)],
+                         ids=["default", "small_chunks", "matvec_only", "min_rows_1"])
+def test_prefill_chunks_with_decode(r, d, opts):
+    """Prefill chunks (causal: each token sees its context up to itself)
+    in the same launch as decode queries; chunk starts and lengths ragged
+    against the 64-token blocks and the tiles' rows."""
+    from workloads import build_mixed
+
+    wl = build_mixed(f"mixed r{r} d{d}", 2 * r, 2, d, "bf16", [(150, 11, (0, 90)), (70, 3, (1, 40))],
+                     [(0, 37), (64, 70), (112, 5), (16, 129)], seed=13)
+    q, k, v = values(wl)
+    _check_full(wl, wl.batch, q, k, v, f"prefill+decode r{r} d{d} {opts}", **opts)
+
+
 # ---------------- edge cases ----------------
 
 def test_stale_padding_is_masked():
@@ -301,7 +317,7 @@ def test_deterministic_and_reusable_workspace():
 
 # ---------------- full-size workloads, sampled ----------------
 
-FULL = ["llama3_8b_8x100", "longchat13b_1x256", "no_sharing_512", "two_level_4x16x16"]
+FULL = ["llama3_8b_8x100", "longchat13b_1x256", "no_sharing_512", "two_level_4x16x16", "mixed_7prefill_256decode"]
 
 
 @pytest.mark.parametrize("name", FULL)

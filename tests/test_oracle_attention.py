@@ -296,3 +296,32 @@ def test_merge_pins_catch_planted_mistakes(mutant, monkeypatch):
     except AssertionError:
         caught = True
     assert caught
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_prefill_chunk_equals_causal_sdpa(seed):
+    """A prefill chunk batched as a group with per-token prefix limits
+    (query_prefix_len) equals the chunk rows of causal attention over the
+    request's whole context: float64 SDPA with is_causal on the full token
+    sequence (library routine), cut to the chunk's rows."""
+    from workloads import build_mixed
+
+    cached, chunk = 32 * (seed + 1), 21 + 7 * seed
+    wl = build_mixed("pf", 8, 2, 64, "f32", [], [(cached, chunk)], seed=seed)
+    q, k, v = make_values(wl, "cpu")
+    q, k, v = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    O, _, _ = oracle.decode_attention(q, k, v, wl.batch)
+    b = wl.batch
+    total = cached + chunk
+    pages = b["group_pages"][b["group_page_off"][0]: b["group_page_off"][1]]
+    r = wl.num_q_heads // wl.num_kv_heads
+    K = np.stack([A.gather_segment(k, pages, total, h, wl.page_size) for h in range(wl.num_kv_heads)])
+    V = np.stack([A.gather_segment(v, pages, total, h, wl.page_size) for h in range(wl.num_kv_heads)])
+    Kt = torch.from_numpy(K).repeat_interleave(r, dim=0)  # [Hq, total, d]
+    Vt = torch.from_numpy(V).repeat_interleave(r, dim=0)
+    # queries for the cached positions do not exist; give them zeros and keep only the chunk rows
+    Q = np.zeros((wl.num_q_heads, total, wl.head_dim))
+    Q[:, cached:] = q.transpose(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(Q), Kt, Vt, is_causal=True,
+                                                           scale=1 / math.sqrt(wl.head_dim))
+    np.testing.assert_allclose(O, ref[:, cached:].numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)

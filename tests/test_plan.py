@@ -62,6 +62,7 @@ def _coverage(wl, plan):
         if g >= 0:
             members.setdefault(int(g), []).append(i)
     member_list = [i for g in sorted(members) for i in members[g]]  # the plan's member array
+    lim = b.get("query_prefix_len")
     items = plan.items()
     assert len(items) % 4 == 0
     for u in range(len(items) // 4):
@@ -91,12 +92,16 @@ def _coverage(wl, plan):
             own = b["group_pages"][b["group_page_off"][ident] + tb // 16: b["group_page_off"][ident] + (te + 15) // 16]
             for mi in range(a // r, (a + bb) // r):
                 qi = member_list[mi]
+                vis = int(lim[qi]) if lim is not None else None
+                if vis is not None and vis <= tb:
+                    continue  # this row's prefix limit ends before the tile: no piece
                 g2 = int(b["query_group"][qi])
                 if g2 != ident:
                     assert g2 > ident and te <= b["group_prefix_len"][g2]
                     other = b["group_pages"][b["group_page_off"][g2] + tb // 16: b["group_page_off"][g2] + (te + 15) // 16]
                     assert list(other) == list(own), (ident, g2, tb, te)
-                cov.setdefault((qi, kvh), []).append(("p", tb, te, kind_full >> 8, None))
+                cov.setdefault((qi, kvh), []).append(("p", tb, te if vis is None else min(te, vis),
+                                                      kind_full >> 8, None))
         elif kind == 3:
             for kvh2 in range(wl.num_kv_heads):
                 cov.setdefault((ident, kvh2), []).append(("e", 0, 0, 0, None))
@@ -112,6 +117,8 @@ def _check_coverage(wl, plan, prefix=True, distinct=True):
     for i in range(wl.num_queries):
         g = int(b["query_group"][i])
         lp = int(b["group_prefix_len"][g]) if g >= 0 else 0
+        if g >= 0 and b.get("query_prefix_len") is not None:
+            lp = int(b["query_prefix_len"][i])
         ld = int(b["query_distinct_len"][i])
         for kvh in range(wl.num_kv_heads):
             parts = cov.get((i, kvh), [])
@@ -502,3 +509,27 @@ def test_peak_entry_points_reject_bad_arguments():
         assert fn(*args) != 0
         assert msg in L.psa_last_error().decode()
 
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_chunks_with_decode_cover_causal_contexts(seed):
+    """Prefill chunks batched with decode queries: every chunk token's
+    prefix pieces cover exactly its causal context [0, cached + t + 1), MFMA
+    tiles stop at their rows' last key, and the mat-vec path clips its items
+    to each query's limit."""
+    from workloads import build_mixed
+
+    rng = np.random.default_rng(seed)
+    prefill = [(int(rng.integers(0, 5)) * 16, int(rng.integers(1, 90))) for _ in range(3)]
+    wl = build_mixed("m", 8, 2, 64, "bf16", [(int(rng.integers(1, 300)), 9, (0, 50))], prefill, seed=seed)
+    b = wl.batch
+    for kw in ({}, {"prefix_chunk_tokens": 32, "mfma_tile_rows": 16}, {"flags": P.FORCE_MATVEC},
+               {"flags": P.PREFIX_ONLY}, {"mfma_min_rows": 1}):
+        plan = P.psa_build_plan(_cfg(wl), b, **kw)
+        _check_coverage(wl, plan, distinct=not kw.get("flags", 0) & P.PREFIX_ONLY)
+        it = plan.items()
+        for row in it[(it[:, 0] & 0xFF) == 2]:
+            assert row[4] <= b["group_prefix_len"][row[2]]
+    bad = dict(b, query_prefix_len=b["query_prefix_len"] + 1)  # past the group prefix
+    with pytest.raises(P.PsaError):
+        P.psa_build_plan(_cfg(wl), bad)

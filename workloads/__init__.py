@@ -13,6 +13,7 @@ from .synth import (  # noqa: F401
     share_leading_pages,
     build_family_case,
     build_token_batch,
+    build_mixed,
     make_values,
     fill_stale,
     algorithmic_cost,

@@ -114,6 +114,29 @@ def share_leading_pages(wl, first, last, pages):
     return wl
 
 
+def build_mixed(name, hq, hkv, d, dtype, decode_groups, prefill, seed=0):
+    """Decode queries and chunks of prefill tokens in one batch.
+
+    ``decode_groups``: as in ``build_single_level``.  ``prefill``: list of
+    (cached, chunk) token counts: a request whose first ``cached`` tokens are
+    already in the KV cache and whose next ``chunk`` tokens (their K/V written
+    too) are being prefilled.  It becomes a group whose prefix is its context
+    [0, cached + chunk) and whose members are the chunk's tokens, token t of
+    the chunk seeing the context up to and including itself
+    (``query_prefix_len`` = cached + t + 1) with no distinct part.
+    """
+    groups = list(decode_groups) + [(c + n, [0] * n) for c, n in prefill]
+    wl = build_single_level(name, hq, hkv, d, dtype, groups, [], seed)
+    b = wl.batch
+    lim = np.asarray(b["group_prefix_len"], dtype=np.int32)[b["query_group"]].copy()
+    base = len(decode_groups)
+    for j, (c, n) in enumerate(prefill):
+        members = np.nonzero(b["query_group"] == base + j)[0]
+        lim[members] = c + 1 + np.arange(n, dtype=np.int32)
+    b["query_prefix_len"] = lim
+    return wl
+
+
 def build_token_batch(n_requests=8000, sharing=3, prefix=(1000, 2100), distinct=(1, 60), system=50, seed=0):
     """Token-id prompts shaped like the pages' industrial summary workload
     (about 3 requests per document, documents of about 1570 tokens, a few
@@ -184,6 +207,11 @@ def build_two_level(name, hq, hkv, d, dtype, n_roots, root_len, n_subs, sub_len,
     return wl
 
 
+def _mixed(seed):
+    return build_mixed("mixed_7prefill_256decode", 32, 8, 128, "bf16", [(2048, 128, (64, 512))] * 2,
+                       [(1024, 512)] * 7, seed)
+
+
 def _tiny_fp32(seed):
     return build_single_level("tiny_fp32_1x4", 2, 1, 64, "f32", [(128, 4, (8, 32))], [], seed)
 
@@ -213,6 +241,7 @@ PRESETS = {
     "longchat13b_1x256": _longchat,
     "no_sharing_512": _nosharing,
     "two_level_4x16x16": _twolevel,
+    "mixed_7prefill_256decode": _mixed,
 }
 
 
@@ -299,9 +328,12 @@ def algorithmic_cost(wl, batch=None):
     kv_distinct = distinct_tok * hkv * d * 2 * e
     q_bytes = n * hq * d * e
     o_bytes = n * hq * d * 4
-    attended = ld + np.where(qg >= 0, lp[np.maximum(qg, 0)] if len(lp) else 0, 0)
+    seen = np.where(qg >= 0, lp[np.maximum(qg, 0)] if len(lp) else 0, 0)
+    if b.get("query_prefix_len") is not None:
+        seen = np.where(qg >= 0, np.minimum(seen, np.asarray(b["query_prefix_len"], dtype=np.int64)), 0)
+    attended = ld + seen
     flops_total = 4 * d * hq * int(attended.sum())
-    flops_prefix = 4 * d * hq * int(np.where(qg >= 0, lp[np.maximum(qg, 0)] if len(lp) else 0, 0).sum())
+    flops_prefix = 4 * d * hq * int(seen.sum())
     return {
         "kv_prefix_bytes": kv_prefix,
         "kv_distinct_bytes": kv_distinct,
@@ -352,6 +384,7 @@ def subset_for_queries(batch, queries):
         g = int(batch["query_group"][i])
         qg.append(gmap[g] if g >= 0 else -1)
         dl.append(int(batch["query_distinct_len"][i]))
+    lim = batch.get("query_prefix_len")
     sub = {
         "page_size": batch["page_size"],
         "group_prefix_len": np.asarray(glen, dtype=np.int32),
@@ -362,6 +395,8 @@ def subset_for_queries(batch, queries):
         "query_page_off": np.asarray(qoff, dtype=np.int64),
         "query_pages": np.asarray(qpages, dtype=np.int32),
     }
+    if lim is not None:
+        sub["query_prefix_len"] = np.asarray([int(lim[i]) for i in queries], dtype=np.int32)
     order = np.empty(len(ids), dtype=np.int64)
     for p, j in ids.items():
         order[j] = p
