@@ -168,6 +168,27 @@ def test_prefill_chunks_with_decode(r, d, opts):
     _check_full(wl, wl.batch, q, k, v, f"prefill+decode r{r} d{d} {opts}", **opts)
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_random_prefix_limits(seed):
+    """Decode queries that see only part of their group's prefix: random
+    limits, including 0 (distinct part only), exact chunk and block
+    boundaries and the whole prefix, with default and small chunks."""
+    rng = np.random.default_rng(70 + seed)
+    wl = build_single_level(f"lim{seed}", 32, 8, 128, "bf16", [(700, 24, (1, 80)), (130, 6, (1, 30))], (2, (1, 50)),
+                            seed=seed)
+    b = wl.batch
+    lp = np.asarray(b["group_prefix_len"])[np.maximum(b["query_group"], 0)]
+    lim = rng.integers(0, lp + 1)
+    picks = [0, 64, 63, 65, 128, 256, 512]
+    for j, v in enumerate(picks):
+        lim[j] = min(v, lp[j])
+    lim[len(picks)] = lp[len(picks)]
+    b["query_prefix_len"] = lim.astype(np.int32)
+    q, k, v = values(wl)
+    for opts in (dict(), dict(prefix_chunk_tokens=128, mfma_tile_rows=32), dict(flags=P.FORCE_MATVEC)):
+        _check_full(wl, b, q, k, v, f"random limits seed {seed} {opts}", **opts)
+
+
 # ---------------- edge cases ----------------
 
 def test_stale_padding_is_masked():
