@@ -37,7 +37,7 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("decode.hip", "psa_internal.h", "plan.cpp"):
+    for f in ("decode.hip", "psa_internal.h", "layout.h", "plan.cpp"):
         with open(os.path.join(ROOT, "prefix_shared_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
