@@ -39,6 +39,8 @@
  *                     slot t % page_size; a (page, kv head) tile is contiguous)
  *   out              [num_queries, num_q_heads, head_dim]        out_dtype
  *   out_m, out_l     [num_queries, num_q_heads]                  float32
+ * Slots of a segment's last page past its length are never read: they may
+ * hold anything, NaN and Inf included.
  */
 #ifndef PSA_H
 #define PSA_H
@@ -166,8 +168,10 @@ psa_status psa_plan_get_info(const psa_plan* plan, psa_plan_info* info);
  * `d_workspace` (>= info.workspace_bytes) on `stream`, and zero its merge
  * counters.  Needed once per (plan, workspace) pair; afterwards the workspace
  * serves any number of psa_decode_attention calls of this plan (counters
- * reset themselves).  The plan must stay alive until the copy has completed
- * (synchronise the stream before psa_destroy_plan). */
+ * reset themselves), until another plan is uploaded into it.  The image
+ * begins with a header naming the plan (a process-unique id).  The plan must
+ * stay alive until the copy has completed (synchronise the stream before
+ * psa_destroy_plan). */
 psa_status psa_plan_upload(psa_plan* plan, void* d_workspace, size_t workspace_bytes,
                            void* stream);
 
@@ -175,7 +179,15 @@ psa_status psa_plan_upload(psa_plan* plan, void* d_workspace, size_t workspace_b
  * d_q / d_k_pool / d_v_pool / d_out: device pointers, layouts above.
  * d_out_m, d_out_l: device pointers or NULL.  d_workspace: the workspace
  * uploaded for this plan.  Concurrent calls on one workspace race (the merge
- * counters live there); use one workspace per stream. */
+ * counters live there); use one workspace per stream.
+ * Errors: PSA_ERR_INVALID_ARGUMENT if `d_workspace` was never uploaded for
+ * this plan on the current device, or another plan was uploaded into it
+ * since.  The kernel also compares the image header with the plan before it
+ * reads anything else from the workspace: if the memory was overwritten
+ * outside the library (e.g. freed and reused), every element of out, out_m
+ * and out_l is set to NaN instead.  (A workspace whose header survived but
+ * whose body was overwritten is not detected: keep it owned while the plan
+ * uses it.) */
 psa_status psa_decode_attention(const psa_plan* plan, const void* d_q, const void* d_k_pool,
                                 const void* d_v_pool, void* d_out, float* d_out_m,
                                 float* d_out_l, void* d_workspace, size_t workspace_bytes,

@@ -1,7 +1,10 @@
 // C ABI of the prefix-shared decode attention library (declared in psa.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <vector>
 #include <cstring>
 #include <new>
 #include <string>
@@ -51,6 +54,51 @@ psa_status set_error(psa_status s, const std::string& msg) {
   g_err = msg;
   return s;
 }
+
+// Which plan's image each (workspace, device) holds: the last upload into it.
+// A decode call must name that plan; an upload of another plan into the same
+// workspace, or the destruction of the plan, invalidates the entry.  (The
+// kernel checks the image header as well, which also catches a workspace
+// overwritten outside the library.)
+namespace {
+struct Upload {
+  uintptr_t ws;
+  int dev;
+  uint32_t plan_id;
+};
+std::mutex g_uploads_mu;
+std::vector<Upload> g_uploads;
+
+void record_upload(uintptr_t ws, int dev, uint32_t plan_id) {
+  std::lock_guard<std::mutex> lk(g_uploads_mu);
+  for (Upload& u : g_uploads)
+    if (u.ws == ws && u.dev == dev) {
+      u.plan_id = plan_id;
+      return;
+    }
+  g_uploads.push_back({ws, dev, plan_id});
+}
+
+// 1: holds this plan's image; 0: never uploaded on this device; -1: holds another plan's image.
+// dev < 0: on any device (1 if some device's copy holds this plan's image).
+int upload_state(uintptr_t ws, int dev, uint32_t plan_id) {
+  std::lock_guard<std::mutex> lk(g_uploads_mu);
+  int state = 0;
+  for (const Upload& u : g_uploads)
+    if (u.ws == ws && (dev < 0 || u.dev == dev)) {
+      if (u.plan_id == plan_id) return 1;
+      state = -1;
+    }
+  return state;
+}
+
+void forget_plan(uint32_t plan_id) {
+  std::lock_guard<std::mutex> lk(g_uploads_mu);
+  g_uploads.erase(std::remove_if(g_uploads.begin(), g_uploads.end(),
+                                 [&](const Upload& u) { return u.plan_id == plan_id; }),
+                  g_uploads.end());
+}
+}  // namespace
 
 }  // namespace psa
 
@@ -114,11 +162,7 @@ psa_status psa_plan_upload(psa_plan* plan, void* d_workspace, size_t bytes, void
                          0x7fc00000u /* quiet NaN */, st);
     if (e != hipSuccess) return psa::hip_fail(e, "poison fill launch");
   }
-  std::lock_guard<std::mutex> lk(plan->mu);
-  const auto key = std::make_pair(reinterpret_cast<uintptr_t>(d_workspace), dev);
-  bool found = false;
-  for (auto& u : plan->uploaded) found = found || u == key;
-  if (!found) plan->uploaded.push_back(key);
+  psa::record_upload(reinterpret_cast<uintptr_t>(d_workspace), dev, plan->id);
   return PSA_OK;
 }
 
@@ -130,20 +174,18 @@ static psa_status decode_impl(const psa_plan* plan, const void* d_q, const void*
   if (bytes < (size_t)L.total_bytes)
     return set_error(PSA_ERR_WORKSPACE_TOO_SMALL,
                      "workspace needs " + std::to_string(L.total_bytes) + " bytes, got " + std::to_string(bytes));
-  auto* mp = const_cast<psa_plan*>(plan);
-  auto uploaded_on = [&](int device, bool any_device) {
-    std::lock_guard<std::mutex> lk(mp->mu);
-    for (auto& u : mp->uploaded)
-      if (u.first == reinterpret_cast<uintptr_t>(d_workspace) && (any_device || u.second == device)) return true;
-    return false;
-  };
-  if (!uploaded_on(0, true))
+  if (psa::upload_state(reinterpret_cast<uintptr_t>(d_workspace), -1, plan->id) == 0)
     return set_error(PSA_ERR_INVALID_ARGUMENT, "workspace was not uploaded for this plan (call psa_plan_upload)");
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return psa::hip_fail(e, "hipGetDevice");
-  if (!uploaded_on(dev, false))
-    return set_error(PSA_ERR_INVALID_ARGUMENT, "workspace was uploaded on another device");
+  const int state = psa::upload_state(reinterpret_cast<uintptr_t>(d_workspace), dev, plan->id);
+  if (state == 0)
+    return set_error(PSA_ERR_INVALID_ARGUMENT,
+                     "workspace was not uploaded for this plan on this device (call psa_plan_upload)");
+  if (state < 0)
+    return set_error(PSA_ERR_INVALID_ARGUMENT,
+                     "workspace holds another plan's upload (call psa_plan_upload for this plan)");
   if (plan->items.empty()) return PSA_OK;
   psa_status s;
   if ((s = psa::check_device_ptr(d_q, "q", dev)) != PSA_OK) return s;
@@ -155,6 +197,9 @@ static psa_status decode_impl(const psa_plan* plan, const void* d_q, const void*
 
   char* ws = static_cast<char*>(d_workspace);
   psa::DecodeParams p{};
+  p.header = reinterpret_cast<const uint32_t*>(ws + L.header);
+  p.plan_id = plan->id;
+  p.num_queries = (int32_t)plan->expected.size();
   p.q = d_q;
   p.k = d_k_pool;
   p.v = d_v_pool;
@@ -273,6 +318,7 @@ void psa_free_batch(psa_batch_owned* o) { delete o; }
 
 void psa_destroy_plan(psa_plan* plan) {
   if (!plan) return;
+  psa::forget_plan(plan->id);
   if (plan->pinned) (void)hipHostFree(plan->pinned);
   delete plan;
 }

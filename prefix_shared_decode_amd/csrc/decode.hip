@@ -59,6 +59,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
+// A wave-uniform float held in a scalar register (the value of the first active lane).
+__device__ __forceinline__ float uniform_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
@@ -221,9 +226,12 @@ __device__ void merge_wave(const DecodeParams& p, int qi, int kvh) {
 // R query heads of the kv head share one read of the page.  Scores are summed
 // over the LPT lanes with DPP; P.V uses bf16 dot2 over pairs of the lane's
 // tokens.  LPT is 8 unless R * dims-per-lane would exceed 64 accumulators.
-// The next page is in flight while one is computed; buffer loads use a descriptor covering one
-// (page, kv head) tile, so a page past the chunk reads zeros with no traffic.  Pages are
-// loaded non-temporal: each byte is read once.
+// The next page is in flight while one is computed; buffer loads use a descriptor covering the
+// valid tokens of one (page, kv head) tile: a page past the chunk, and the slots past the
+// chunk's end in its last page, read zeros with no traffic (so whatever those slots hold, NaN
+// included, never meets a weight).  Pages are loaded non-temporal: each byte is read once.
+// P is rounded to bf16 for the P.V dot products; O is normalised by the sum of those rounded
+// weights (a convex combination of V rows), while the reported l is the exact fp32 sum.
 // q is staged once through LDS (per wave) and re-read per page.
 template <int D, int R, bool BF16>
 struct MvShape {
@@ -253,7 +261,7 @@ __device__ __forceinline__ float sum_lanes(float v) {
 }
 
 template <int D, int R, bool BF16>
-__device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* smem) {
+__device__ __forceinline__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* smem) {
   using S = MvShape<D, R, BF16>;
   constexpr int NCH = S::NCH, EPC = S::EPC, DPL = S::DPL, LPT = S::LPT, NT = S::NT, TSTEP = S::TSTEP;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -261,6 +269,7 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
   const int qi = it.id, kvh = it.kvh;
   const int tb = it.tok_begin, te = it.tok_end;
   const int npages = (te - tb + 15) >> 4;
+  const uint32_t last_bytes = (uint32_t)(te - tb - 16 * (npages - 1)) * (D * S::EB);  // valid part of the last page
   const int pid_lane = lane < npages ? p.pages[it.page_base + lane] : 0;
 
   // stage this wave's q rows (R * D elements, contiguous) in LDS
@@ -270,7 +279,7 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
     for (int o16 = lane; o16 < S::QBYTES / 16; o16 += 64)
       *(__attribute__((address_space(3))) u32x4*)(qs + o16 * 16) = *reinterpret_cast<const u32x4*>(qg + o16 * 16);
   }
-  float mref[R], mtrue[R], l[R], o[R][DPL];
+  float mref[R], mtrue[R], l[R], lr[R], o[R][DPL];  // l: exact weights; lr: their bf16 roundings
   const float sc = p.scale_log2;
   const char* kpool = reinterpret_cast<const char*>(p.k);
   const char* vpool = reinterpret_cast<const char*>(p.v);
@@ -279,8 +288,9 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
     // j beyond the chunk: an empty descriptor reads zeros without memory traffic
     const int pid = __builtin_amdgcn_readlane(pid_lane, j < npages ? j : 0);
     const int64_t tile = ((int64_t)pid * p.hkv + kvh) * S::TILE;
-    const auto rk = make_rsrc(kpool + tile, j < npages ? S::TILE : 0u);
-    const auto rv = make_rsrc(vpool + tile, j < npages ? S::TILE : 0u);
+    const uint32_t bytes = j < npages - 1 ? S::TILE : (j == npages - 1 ? last_bytes : 0u);
+    const auto rk = make_rsrc(kpool + tile, bytes);
+    const auto rv = make_rsrc(vpool + tile, bytes);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -291,11 +301,14 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
       }
   };
 
-  // scores of page j (log2 units, masked tokens -inf)
-  auto scores = [&](const PageRegs<D, R, BF16>& b, int j, float (&s)[NT][R]) {
+  // Page j, one head at a time (so only NT scores are live): the scores (log2
+  // units, masked tokens -inf); on the first page of the first pass, the
+  // head's reference max; the exponentials against it; P.V.
+  auto page = [&](const PageRegs<D, R, BF16>& b, int j, bool set_ref, bool& over) {
     // re-read q from LDS every page (an opaque offset keeps the reads in the loop)
     uint32_t qoff = (uint32_t)(c * EPC * S::EB);
     asm volatile("" : "+v"(qoff));
+    const int tok0 = tb + j * 16 + ts;
 #pragma unroll
     for (int h = 0; h < R; ++h) {
       float acc[NT];
@@ -314,34 +327,31 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
               acc[t] = fmaf(__uint_as_float(b.k[t][k][w]), __uint_as_float(qv[w]), acc[t]);
           }
       }
+      float sh[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) s[t][h] = sum_lanes<LPT>(acc[t]);
-    }
-    const int tok0 = tb + j * 16 + ts;
+      for (int t = 0; t < NT; ++t) sh[t] = tok0 + TSTEP * t < te ? sum_lanes<LPT>(acc[t]) * sc : -INFINITY;
+      if (set_ref) {
+        float mx = sh[0];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const bool ok = tok0 + TSTEP * t < te;
-#pragma unroll
-      for (int h = 0; h < R; ++h) s[t][h] = ok ? s[t][h] * sc : -INFINITY;
-    }
-  };
-
-  // exponentials against the fixed reference max, then P.V
-  auto accumulate = [&](const PageRegs<D, R, BF16>& b, const float (&s)[NT][R], bool& over) {
-#pragma unroll
-    for (int h = 0; h < R; ++h) {
+        for (int t = 1; t < NT; ++t) mx = fmaxf(mx, sh[t]);
+        mx = fmaxf(mx, xor8(mx));
+        mx = max_lane_groups(mx);  // page 0 always holds a valid token
+        mref[h] = uniform_f(mx);   // the max over every token slot of the page: the same in each lane
+        mtrue[h] = -INFINITY;
+      }
       float pr[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        mtrue[h] = fmaxf(mtrue[h], s[t][h]);
-        over |= s[t][h] > mref[h] + kSlack;
-        pr[t] = fast_exp2(s[t][h] - mref[h]);  // exp2(-inf) = 0 for masked tokens
+        mtrue[h] = fmaxf(mtrue[h], sh[t]);
+        over |= sh[t] > mref[h] + kSlack;
+        pr[t] = fast_exp2(sh[t] - mref[h]);  // exp2(-inf) = 0 for masked tokens
         l[h] += pr[t];
       }
       if constexpr (BF16) {
 #pragma unroll
         for (int t = 0; t < NT; t += 2) {
           const uint32_t pp = pack_bf16(pr[t], pr[t + 1]);
+          lr[h] = dot2_bf16(pp, 0x3F803F80u, lr[h]);  // + the two rounded weights (times bf16 1.0)
 #pragma unroll
           for (int k = 0; k < NCH; ++k)
 #pragma unroll
@@ -383,6 +393,7 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
 #pragma unroll
     for (int h = 0; h < R; ++h) {
       l[h] = 0.f;
+      lr[h] = 0.f;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
     }
@@ -392,34 +403,14 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
     PageRegs<D, R, BF16> b[kMvPages];
 #pragma unroll
     for (int u = 0; u < kMvPages; ++u) load(b[u], u);
-    {
-      float s[NT][R];
-      scores(b[0], 0, s);
-      if (!fixed_ref) {
-#pragma unroll
-        for (int h = 0; h < R; ++h) {
-          float mx = s[0][h];
-#pragma unroll
-          for (int t = 1; t < NT; ++t) mx = fmaxf(mx, s[t][h]);
-          mx = fmaxf(mx, xor8(mx));
-          mx = max_lane_groups(mx);  // page 0 always holds a valid token
-          mref[h] = mx;
-          mtrue[h] = -INFINITY;
-        }
-      }
-      accumulate(b[0], s, over);
-    }
+    page(b[0], 0, !fixed_ref, over);
     load(b[0], kMvPages);
     for (int j = 1; j < npages; j += kMvPages) {
       if (!ctr_read && j + kMvPages >= npages) read_ctr();
 #pragma unroll
       for (int u = 0; u < kMvPages; ++u) {
         const int bi = (u + 1) % kMvPages;
-        if (j + u < npages) {  // wave-uniform; loads past the end read zeros without traffic
-          float s1[NT][R];
-          scores(b[bi], j + u, s1);
-          accumulate(b[bi], s1, over);
-        }
+        if (j + u < npages) page(b[bi], j + u, false, over);  // wave-uniform; loads past the end read zeros
         load(b[bi], j + u + kMvPages);
       }
     }
@@ -431,32 +422,34 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
       float mx = mtrue[h];
       mx = fmaxf(mx, xor8(mx));
       mx = max_lane_groups(mx);
-      mref[h] = mx;
+      mref[h] = uniform_f(mx);
     }
     fixed_ref = true;
   }
 
-  // merge the token groups (lanes with equal lane % LPT): a symmetric merge
-  // of each lane's state with its partner's at distance 8 (DPP), 16 and 32
-  // (permlane swaps), all in VALU
+  // merge the token groups (lanes with equal lane % LPT): each lane's state
+  // with its partner's at distance 8 (DPP), 16 and 32 (permlane swaps), all
+  // in VALU.  Every lane's weights are relative to the same wave-uniform
+  // reference max, so merging two lanes' states is a plain sum.
   auto merge_step = [&](auto off_tag) {
     constexpr int OFF = decltype(off_tag)::value;
 #pragma unroll
     for (int h = 0; h < R; ++h) {
-      float m0, m1, l0, l1, t0, t1;
-      lane_pair<OFF>(mref[h], m0, m1);
+      float l0, l1, t0, t1;
       lane_pair<OFF>(l[h], l0, l1);
       lane_pair<OFF>(mtrue[h], t0, t1);
-      const float M = fmaxf(m0, m1);
-      const float a = fast_exp2(m0 - M), bw = fast_exp2(m1 - M);
-      l[h] = l0 * a + l1 * bw;
+      l[h] = l0 + l1;
+      if constexpr (BF16) {
+        float r0, r1;
+        lane_pair<OFF>(lr[h], r0, r1);
+        lr[h] = r0 + r1;
+      }
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         float o0, o1;
         lane_pair<OFF>(o[h][e], o0, o1);
-        o[h][e] = o0 * a + o1 * bw;
+        o[h][e] = o0 + o1;
       }
-      mref[h] = M;
       mtrue[h] = fmaxf(t0, t1);
     }
   };
@@ -464,11 +457,12 @@ __device__ void matvec_wave(const DecodeParams& p, const WorkItem& it, char* sme
   merge_step(std::integral_constant<int, 16>{});
   merge_step(std::integral_constant<int, 32>{});
 
-  // lanes 0..LPT-1 hold the result: O normalised, m (true max), l relative to it
+  // lanes 0..LPT-1 hold the result: O normalised (by the weights P.V used), m (true max), the
+  // exact l relative to it
   float inv[R], lt[R];
 #pragma unroll
   for (int h = 0; h < R; ++h) {
-    inv[h] = 1.f / l[h];
+    inv[h] = 1.f / (BF16 ? lr[h] : l[h]);
     lt[h] = l[h] * fast_exp2(mref[h] - mtrue[h]);
   }
   const bool last_by_count = E > 1 && __builtin_amdgcn_readfirstlane(cval) == E - 1;
@@ -862,7 +856,7 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
 }
 
 template <int D, int R>
-__device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_char* stage0, lds_char* stage1) {
+__device__ __forceinline__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_char* stage0, lds_char* stage1) {
   using S = MfShape<D>;
   constexpr int KK = S::KK, NB = S::NB, NI = S::NI;
   constexpr int ROW = MfLayout<D>::ROW, TILEB = 16 * D * 2;  // bytes of one (page, kv head) tile
@@ -1213,13 +1207,32 @@ __device__ void prefix_mfma_tile(const DecodeParams& p, const WorkItem& it, lds_
 // Empty partial (0, -inf, 0) of every head of a query the plan does not
 // cover (PREFIX_ONLY / DISTINCT_ONLY plans); one wave.
 template <int D>
-__device__ void empty_wave(const DecodeParams& p, const WorkItem& it) {
+__device__ __forceinline__ void empty_wave(const DecodeParams& p, const WorkItem& it) {
   const int lane = threadIdx.x & 63;
   const int64_t base = (int64_t)it.id * p.hq;
   for (int el = lane * 4; el < p.hq * D; el += 256) store_out4(p, base * D + el, f32x4{0.f, 0.f, 0.f, 0.f});
   for (int h = lane; h < p.hq; h += 64) {
     if (p.out_m) p.out_m[base + h] = -INFINITY;
     if (p.out_l) p.out_l[base + h] = 0.f;
+  }
+}
+
+// The workspace does not hold the launching plan's image (overwritten since
+// its upload): every output element becomes NaN, so the failure is loud, and
+// nothing else is read from the workspace.  Grid-stride over the outputs.
+template <int D>
+__device__ __forceinline__ void poison_outputs(const DecodeParams& p) {
+  const int64_t rows = (int64_t)p.num_queries * p.hq;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows * D; i += stride) {
+    if (p.out_bf16)
+      reinterpret_cast<uint16_t*>(p.out)[i] = 0x7fc0u;
+    else
+      reinterpret_cast<float*>(p.out)[i] = __builtin_nanf("");
+    if (i < rows) {
+      if (p.out_m) p.out_m[i] = __builtin_nanf("");
+      if (p.out_l) p.out_l[i] = __builtin_nanf("");
+    }
   }
 }
 
@@ -1239,7 +1252,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lds1[Lds<D, R, BF16>::MF];
   const uint64_t t0 = p.trace ? __builtin_amdgcn_s_memrealtime() : 0;
   const WorkItem* unit = p.items + (int64_t)blockIdx.x * kUnitItems;
-  const int kind0 = unit[0].kind & 0xff;
+  // the image header and this unit's first word load together (scalar loads, one wait)
+  const uint64_t hdr = *reinterpret_cast<const uint64_t*>(p.header);
+  const int word0 = unit[0].kind;
+  asm volatile("" ::"s"(hdr), "s"(word0));
+  if (hdr != (((uint64_t)p.plan_id << 32) | kImageMagic)) {
+    poison_outputs<D>(p);
+    return;
+  }
+  const int kind0 = word0 & 0xff;
   if (kind0 == ITEM_PREFIX_MFMA) {
     if constexpr (BF16)
       prefix_mfma_tile<D, R>(p, unit[0], (lds_char*)lds0, (lds_char*)lds1);

@@ -11,6 +11,7 @@
 //    distinct parts, split the long KV range (split-K) so the work balances.
 //  * §3.2 Eq. 2: saved tokens = logical - processed.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <limits>
@@ -24,6 +25,15 @@ namespace psa {
 namespace {
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Process-unique plan ids (never 0), written into each plan's workspace image.
+uint32_t next_plan_id() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t id;
+  do id = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  while (id == 0);
+  return id;
+}
 int64_t ceil_div(int64_t x, int64_t a) { return (x + a - 1) / a; }
 
 psa_status check_segment(const char* what, int64_t idx, int64_t len, int64_t off_a, int64_t off_b,
@@ -495,6 +505,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     off = round_up(off + bytes, 256);
     return at;
   };
+  L.header = sect(8);
   L.items = sect((int64_t)items.size() * (int64_t)sizeof(WorkItem));
   L.pages = sect((n_gpages + n_qpages) * 4);
   L.member_off = sect((G + 1) * 4);
@@ -528,6 +539,9 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     int32_t x = (int32_t)v;
     std::memcpy(img.data() + at + idx * 4, &x, 4);
   };
+  plan->id = next_plan_id();
+  const uint32_t header[2] = {kImageMagic, plan->id};
+  std::memcpy(img.data() + L.header, header, sizeof(header));
   if (!items.empty()) std::memcpy(img.data() + L.items, items.data(), items.size() * sizeof(WorkItem));
   for (int64_t t = 0; t < n_gpages; ++t) put32(L.pages, t, b->group_pages[t]);
   for (int64_t t = 0; t < n_qpages; ++t) put32(L.pages, n_gpages + t, b->query_pages[t]);

@@ -23,10 +23,10 @@ struct psa_plan {
   uint32_t part_o_bytes = 0, part_ml_bytes = 0;
   std::vector<int32_t> expected;       // per query
   std::vector<int32_t> slot_off;       // per query (-1: written directly)
+  uint32_t id = 0;                     // process-unique; also in the image header
   // pinned staging buffer for the upload, allocated on first upload
   void* pinned = nullptr;
   std::mutex mu;
-  std::vector<std::pair<uintptr_t, int>> uploaded;  // (workspace, device) pairs
 };
 
 struct psa_batch_owned {

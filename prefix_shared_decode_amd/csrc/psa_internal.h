@@ -34,9 +34,15 @@ constexpr int kUnitItems = 4;
 constexpr int kMaxMatvecPages = 64;   // a mat-vec chunk holds at most 64 pages (1024 tokens)
 constexpr int kMaxPrefixChunk = 2048; // tokens per MFMA prefix chunk (page ids staged in LDS)
 
+// First 8 bytes of a workspace image: a magic word and the id of the plan
+// that uploaded it.  The kernel compares them with the launching plan's id
+// before it reads anything else from the workspace.
+constexpr uint32_t kImageMagic = 0x31415350u;  // "PSA1"
+
 // Device image of a plan: the workspace begins with these arrays, at the
 // byte offsets the plan records (int32 everywhere on the device).
 struct ImageLayout {
+  int64_t header;  // {kImageMagic, plan id}
   int64_t items, pages, member_off, members, expected, slot_off;
   int64_t qlim;  // visible prefix tokens per query, -1 = no limits (every query sees its whole prefix)
   int64_t counters, part_o, part_ml;
@@ -46,6 +52,7 @@ struct ImageLayout {
 
 // Launch arguments of the fused kernel (passed by value).
 struct DecodeParams {
+  const uint32_t* header;   // workspace image header: {kImageMagic, plan_id}
   const void* q;
   const void* k;
   const void* v;
@@ -65,6 +72,8 @@ struct DecodeParams {
   uint32_t part_o_bytes;
   uint32_t part_ml_bytes;
   int32_t num_units;
+  uint32_t plan_id;         // id of the launching plan (must match the image header)
+  int32_t num_queries;
   int32_t hq;
   int32_t hkv;
   float scale_log2;         // sm_scale * log2(e)

@@ -12,7 +12,7 @@ import numpy as np
 
 import oracle
 import prefix_shared_decode_amd as P
-from workloads import make_values, subset_for_queries
+from workloads import make_values
 
 # parity tolerances (bf16 inputs; fp32 inputs), over the whole output tensor
 TOL = {"bf16": {"max_abs": 1e-2, "rel_l2": 5e-3}, "f32": {"max_abs": 1e-5, "rel_l2": 1e-5}}
@@ -75,21 +75,6 @@ def assert_lse_close(m, l, M, L, tol):
     err = float(np.abs(got - ref).max())
     log(f"  lse max err {err:.3e}")
     assert err <= tol
-
-
-def sampled_oracle(wl, batch, q, k, v, queries, heads=None):
-    """Oracle on a subset of queries, copying only their pages off the GPU."""
-    import torch
-
-    sub, page_ids = subset_for_queries(batch, queries)
-    idx = torch.as_tensor(page_ids, device=k.device, dtype=torch.long)
-    ks = to_host64(k.index_select(0, idx))
-    vs = to_host64(v.index_select(0, idx))
-    qs = to_host64(q.index_select(0, torch.as_tensor(list(queries), device=q.device, dtype=torch.long)))
-    if heads is None:
-        return oracle.decode_attention(qs, ks, vs, sub)
-    pairs = [(j, h) for j in range(len(queries)) for h in heads]
-    return oracle.decode_attention_rows(qs, ks, vs, sub, pairs)
 
 
 def scale_default(d):

@@ -360,6 +360,26 @@ def test_flatten_two_level_workload_closed_form():
     assert info["saved_tokens"] == saved
 
 
+def test_flatten_two_level_workload_keeps_every_context():
+    """The library's flattening of the full two-level workload (the batch the
+    kernel runs at full size) keeps each query's tokens: group prefix pages ++
+    own pages name the tree's root-to-query pages in order, with the same
+    token count."""
+    from workloads import make_workload
+
+    wl = make_workload("two_level_4x16x16")
+    t = wl.tree
+    batch, _ = P.psa_flatten_prefix_tree(t)
+    for i in range(len(t["query_node"])):
+        pages, n = _tree_context(t, i)
+        flat, total = [], 0
+        for p, ln in oracle.query_context(batch, i):
+            flat += [int(x) for x in p[: -(-ln // 16)]]
+            total += ln
+        assert total == n
+        assert flat == [int(x) for x in pages[: -(-n // 16)]]
+
+
 def test_flatten_error_paths():
     t = _random_tree(3)
     assert _status(lambda: P.psa_flatten_prefix_tree(dict(t, node_len=[x + 1 for x in t["node_len"]]))) == \
