@@ -146,6 +146,8 @@ typedef struct {
   double prefix_flops;       /* part of algorithmic_flops on prefix tokens */
   double prefix_kv_bytes;    /* prefix KV bytes, once per group */
   double distinct_kv_bytes;  /* distinct KV bytes */
+  size_t image_bytes;        /* leading part of the workspace that psa_plan_upload fills (the
+                                plan image); what psa_decode_attention_noalloc needs */
 } psa_plan_info;
 
 typedef struct psa_plan psa_plan;
@@ -165,8 +167,9 @@ psa_status psa_build_plan(const psa_config* cfg, const psa_batch* batch,
 psa_status psa_plan_get_info(const psa_plan* plan, psa_plan_info* info);
 
 /* Copy the plan's work list and page tables into the device workspace
- * `d_workspace` (>= info.workspace_bytes) on `stream`, and zero its merge
- * counters.  Needed once per (plan, workspace) pair; afterwards the workspace
+ * `d_workspace` on `stream`, and zero its merge counters.  The workspace must
+ * hold info.workspace_bytes for psa_decode_attention, or at least
+ * info.image_bytes for psa_decode_attention_noalloc.  Needed once per (plan, workspace) pair; afterwards the workspace
  * serves any number of psa_decode_attention calls of this plan (counters
  * reset themselves), until another plan is uploaded into it.  The image
  * begins with a header naming the plan (a process-unique id).  The plan must
@@ -192,6 +195,25 @@ psa_status psa_decode_attention(const psa_plan* plan, const void* d_q, const voi
                                 const void* d_v_pool, void* d_out, float* d_out_m,
                                 float* d_out_l, void* d_workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* psa_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, with their scratch (the merge counters and the fp32
+ * partial results) in a static device array of the library, 64 MiB per GPU,
+ * held until the process ends.  `d_image` is a buffer into which
+ * psa_plan_upload copied this plan (>= info.image_bytes; the rest of the
+ * workspace is not needed).  The call clears the counters with a fill kernel
+ * and launches the decode on `stream`; it allocates nothing and calls no
+ * allocating routine.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (different streams, or host threads) race.
+ * Errors: PSA_ERR_WORKSPACE_TOO_SMALL if the plan needs more scratch than the
+ * array holds (info.workspace_bytes - info.image_bytes > 64 MiB, e.g. very many
+ * partial results; use psa_decode_attention with a workspace then) or
+ * image_bytes < info.image_bytes; otherwise as psa_decode_attention. */
+psa_status psa_decode_attention_noalloc(const psa_plan* plan, const void* d_q, const void* d_k_pool,
+                                        const void* d_v_pool, void* d_out, float* d_out_m,
+                                        float* d_out_l, const void* d_image, size_t image_bytes,
+                                        void* stream);
 
 /* Eq. 1's online_softmax merge of two partial results, elementwise over `rows`
  * rows of `head_dim` (a power of two in [4, 256]):

@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     psa_debug_mfma_peak,
     psa_debug_read_peak,
     psa_decode_attention,
+    psa_decode_attention_noalloc,
     psa_flatten_prefix_tree,
     psa_identify_prefix_groups,
     psa_merge,

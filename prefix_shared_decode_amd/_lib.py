@@ -27,7 +27,8 @@ EXPORTS = ["psa_build_plan", "psa_plan_get_info", "psa_plan_upload", "psa_decode
            "psa_flatten_prefix_tree", "psa_batch_owned_view", "psa_free_batch", "psa_destroy_plan",
            "psa_last_error", "psa_version", "psa_plan_debug_items", "psa_plan_debug_queries",
            "psa_decode_attention_traced", "psa_debug_read_peak", "psa_debug_mfma_peak",
-           "psa_identify_prefix_groups", "psa_prefix_groups_view", "psa_free_prefix_groups"]
+           "psa_identify_prefix_groups", "psa_prefix_groups_view", "psa_free_prefix_groups",
+           "psa_decode_attention_noalloc"]
 
 
 class PsaError(RuntimeError):
@@ -65,7 +66,7 @@ class psa_plan_info(C.Structure):
                 ("num_matvec_items", C.c_int64), ("num_partial_slots", C.c_int64), ("logical_tokens", C.c_int64),
                 ("processed_tokens", C.c_int64), ("saved_tokens", C.c_int64), ("algorithmic_bytes", C.c_double),
                 ("algorithmic_flops", C.c_double), ("prefix_flops", C.c_double), ("prefix_kv_bytes", C.c_double),
-                ("distinct_kv_bytes", C.c_double)]
+                ("distinct_kv_bytes", C.c_double), ("image_bytes", C.c_size_t)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -99,6 +100,7 @@ def lib():
         L.psa_plan_get_info.argtypes = [vp, C.POINTER(psa_plan_info)]
         L.psa_plan_upload.argtypes = [vp, vp, C.c_size_t, vp]
         L.psa_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.psa_decode_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.psa_merge.argtypes = [C.c_int64, C.c_int32] + [vp] * 9 + [vp]
         L.psa_flatten_prefix_tree.argtypes = [C.POINTER(psa_tree), C.c_int32, C.POINTER(vp)]
         L.psa_batch_owned_view.argtypes = [vp, C.POINTER(psa_batch), _I64P]
@@ -254,12 +256,7 @@ def psa_plan_upload(plan, workspace, stream=None):
                                  workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
 
 
-def psa_decode_attention(plan, q, k_pool, v_pool, out, workspace, out_m=None, out_l=None, stream=None, trace=None):
-    """One fused decode launch; shapes/dtypes are checked against the plan's config.
-
-    trace: optional int64 device tensor of >= 4 * num_items entries; the launch
-    then records per-unit timing (include/psa_debug.h psa_decode_attention_traced).
-    """
+def _check_io(plan, q, k_pool, v_pool, out, out_m, out_l):
     import torch
 
     cfg = plan.cfg
@@ -275,6 +272,17 @@ def psa_decode_attention(plan, q, k_pool, v_pool, out, workspace, out_m=None, ou
     for name, t in (("out_m", out_m), ("out_l", out_l)):
         if t is not None and (tuple(t.shape) != (n, cfg.num_q_heads) or t.dtype != torch.float32):
             raise ValueError(f"{name}: expected {(n, cfg.num_q_heads)} float32")
+
+
+def psa_decode_attention(plan, q, k_pool, v_pool, out, workspace, out_m=None, out_l=None, stream=None, trace=None):
+    """One fused decode launch; shapes/dtypes are checked against the plan's config.
+
+    trace: optional int64 device tensor of >= 4 * num_items entries; the launch
+    then records per-unit timing (include/psa_debug.h psa_decode_attention_traced).
+    """
+    import torch
+
+    _check_io(plan, q, k_pool, v_pool, out, out_m, out_l)
     args = (plan.handle, _dev_ptr(q, "q"), _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"),
             _dev_ptr(out, "out"), _dev_ptr(out_m, "out_m"), _dev_ptr(out_l, "out_l"),
             _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size())
@@ -284,6 +292,16 @@ def psa_decode_attention(plan, q, k_pool, v_pool, out, workspace, out_m=None, ou
         if trace.dtype != torch.int64:
             raise ValueError("trace: expected an int64 tensor")
         _check(lib().psa_decode_attention_traced(*args, _dev_ptr(trace, "trace"), trace.numel(), _stream_ptr(stream)))
+
+
+def psa_decode_attention_noalloc(plan, q, k_pool, v_pool, out, image, out_m=None, out_l=None, stream=None):
+    """psa_decode_attention with the library's static scratch (allocates nothing);
+    ``image`` is a device buffer into which psa_plan_upload copied this plan."""
+    _check_io(plan, q, k_pool, v_pool, out, out_m, out_l)
+    _check(lib().psa_decode_attention_noalloc(
+        plan.handle, _dev_ptr(q, "q"), _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), _dev_ptr(out, "out"),
+        _dev_ptr(out_m, "out_m"), _dev_ptr(out_l, "out_l"), _dev_ptr(image, "image"),
+        image.numel() * image.element_size(), _stream_ptr(stream)))
 
 
 def psa_debug_read_peak(buf, sink, stream=None):

@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           f"-I{os.path.join(ROOT, 'include')}"]
 
-SOURCES = ["abi.cpp", "plan.cpp", "flatten.cpp", "identify.cpp", "decode.hip", "merge.hip", "peaks.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "flatten.cpp", "identify.cpp", "decode.hip", "merge.hip", "peaks.hip", "noalloc.hip"]
 
 
 def _compile(src: str) -> str:

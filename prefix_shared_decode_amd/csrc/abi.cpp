@@ -131,9 +131,9 @@ psa_status psa_plan_get_info(const psa_plan* plan, psa_plan_info* info) {
 
 psa_status psa_plan_upload(psa_plan* plan, void* d_workspace, size_t bytes, void* stream) {
   if (!plan) return set_error(PSA_ERR_INVALID_ARGUMENT, "plan is NULL");
-  if (bytes < (size_t)plan->layout.total_bytes)
-    return set_error(PSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(plan->layout.total_bytes) +
-                                                      " bytes, got " + std::to_string(bytes));
+  if (bytes < (size_t)plan->layout.meta_bytes)
+    return set_error(PSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(plan->layout.meta_bytes) +
+                                                      " bytes for the plan image, got " + std::to_string(bytes));
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return psa::hip_fail(e, "hipGetDevice");
@@ -166,14 +166,24 @@ psa_status psa_plan_upload(psa_plan* plan, void* d_workspace, size_t bytes, void
   return PSA_OK;
 }
 
-static psa_status decode_impl(const psa_plan* plan, const void* d_q, const void* d_k_pool, const void* d_v_pool,
-                              void* d_out, float* d_out_m, float* d_out_l, void* d_workspace, size_t bytes,
-                              uint64_t* d_trace, void* stream) {
+}  // extern "C"
+
+namespace psa {
+// The fused launch.  scratch == nullptr: counters and partials live in the
+// workspace after the image (which then needs layout.total_bytes); otherwise
+// they live at `scratch` (layout.total_bytes - layout.counters bytes, the
+// caller checked the size), the workspace holds only the image, and the
+// counters are cleared by a fill kernel first.
+psa_status decode_impl(const psa_plan* plan, const void* d_q, const void* d_k_pool, const void* d_v_pool,
+                       void* d_out, float* d_out_m, float* d_out_l, const void* d_workspace, size_t bytes,
+                       uint64_t* d_trace, void* stream, char* scratch) {
   if (!plan) return set_error(PSA_ERR_INVALID_ARGUMENT, "plan is NULL");
   const psa::ImageLayout& L = plan->layout;
-  if (bytes < (size_t)L.total_bytes)
+  const int64_t need = scratch ? L.meta_bytes : L.total_bytes;
+  if (bytes < (size_t)need)
     return set_error(PSA_ERR_WORKSPACE_TOO_SMALL,
-                     "workspace needs " + std::to_string(L.total_bytes) + " bytes, got " + std::to_string(bytes));
+                     std::string(scratch ? "plan image needs " : "workspace needs ") + std::to_string(need) +
+                         " bytes, got " + std::to_string(bytes));
   if (psa::upload_state(reinterpret_cast<uintptr_t>(d_workspace), -1, plan->id) == 0)
     return set_error(PSA_ERR_INVALID_ARGUMENT, "workspace was not uploaded for this plan (call psa_plan_upload)");
   int dev = 0;
@@ -195,7 +205,7 @@ static psa_status decode_impl(const psa_plan* plan, const void* d_q, const void*
   if (d_out_m && (s = psa::check_device_ptr(d_out_m, "out_m", dev)) != PSA_OK) return s;
   if (d_out_l && (s = psa::check_device_ptr(d_out_l, "out_l", dev)) != PSA_OK) return s;
 
-  char* ws = static_cast<char*>(d_workspace);
+  char* ws = static_cast<char*>(const_cast<void*>(d_workspace));
   psa::DecodeParams p{};
   p.header = reinterpret_cast<const uint32_t*>(ws + L.header);
   p.plan_id = plan->id;
@@ -213,9 +223,12 @@ static psa_status decode_impl(const psa_plan* plan, const void* d_q, const void*
   p.expected = reinterpret_cast<const int32_t*>(ws + L.expected);
   p.slot_off = reinterpret_cast<const int32_t*>(ws + L.slot_off);
   p.qlim = L.qlim >= 0 ? reinterpret_cast<const int32_t*>(ws + L.qlim) : nullptr;
-  p.counters = reinterpret_cast<int32_t*>(ws + L.counters);
-  p.part_o = reinterpret_cast<float*>(ws + L.part_o);
-  p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+  // counters and partials: after the image in the workspace, or at the start of the scratch array
+  // (same relative offsets, all 256-byte aligned)
+  char* cbase = scratch ? scratch : ws + L.counters;
+  p.counters = reinterpret_cast<int32_t*>(cbase);
+  p.part_o = reinterpret_cast<float*>(cbase + (L.part_o - L.counters));
+  p.part_ml = reinterpret_cast<float*>(cbase + (L.part_ml - L.counters));
   p.part_o_bytes = plan->part_o_bytes;
   p.part_ml_bytes = plan->part_ml_bytes;
   p.num_units = (int32_t)plan->num_units;
@@ -224,16 +237,25 @@ static psa_status decode_impl(const psa_plan* plan, const void* d_q, const void*
   p.scale_log2 = plan->sm_scale * 1.4426950408889634f;
   p.out_bf16 = plan->cfg.out_dtype == PSA_BF16;
   p.trace = d_trace;
+  if (scratch) {  // the array keeps the last call's contents: counters must start at zero
+    e = psa::launch_fill(reinterpret_cast<uint32_t*>(p.counters), (int64_t)p.num_queries * p.hkv, 0u,
+                         reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return psa::hip_fail(e, "counter clear launch");
+  }
   e = psa::launch_decode(p, plan->cfg.head_dim, plan->r, plan->cfg.kv_dtype == PSA_BF16,
                          reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return psa::hip_fail(e, "decode kernel launch");
   return PSA_OK;
 }
+}  // namespace psa
+
+extern "C" {
 
 psa_status psa_decode_attention(const psa_plan* plan, const void* d_q, const void* d_k_pool, const void* d_v_pool,
                                 void* d_out, float* d_out_m, float* d_out_l, void* d_workspace, size_t bytes,
                                 void* stream) {
-  return decode_impl(plan, d_q, d_k_pool, d_v_pool, d_out, d_out_m, d_out_l, d_workspace, bytes, nullptr, stream);
+  return psa::decode_impl(plan, d_q, d_k_pool, d_v_pool, d_out, d_out_m, d_out_l, d_workspace, bytes, nullptr, stream,
+                           nullptr);
 }
 
 psa_status psa_decode_attention_traced(const psa_plan* plan, const void* d_q, const void* d_k_pool,
@@ -252,8 +274,8 @@ psa_status psa_decode_attention_traced(const psa_plan* plan, const void* d_q, co
     psa_status s = psa::check_device_ptr(d_trace, "trace", dev);
     if (s != PSA_OK) return s;
   }
-  return decode_impl(plan, d_q, d_k_pool, d_v_pool, d_out, d_out_m, d_out_l, d_workspace, bytes,
-                     static_cast<uint64_t*>(d_trace), stream);
+  return psa::decode_impl(plan, d_q, d_k_pool, d_v_pool, d_out, d_out_m, d_out_l, d_workspace, bytes,
+                          static_cast<uint64_t*>(d_trace), stream, nullptr);
 }
 
 psa_status psa_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* m_a, const float* l_a,

@@ -586,6 +586,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
                            (double)N * c.num_q_heads * d * (c.out_dtype == PSA_BF16 ? 2 : 4);
   info.algorithmic_flops = 4.0 * d * c.num_q_heads * (double)logical;
   info.prefix_flops = 4.0 * d * c.num_q_heads * (double)prefix_logical;
+  info.image_bytes = (size_t)L.meta_bytes;
 
   plan->items = std::move(items);
   plan->expected = std::move(expected);

@@ -269,7 +269,7 @@ def test_decode_rejects_host_pointers_and_small_workspace_without_launching():
     st = L.psa_decode_attention(plan.handle, C.addressof(host), C.addressof(host), C.addressof(host),
                                 C.addressof(host), None, None, C.addressof(host), ws_bytes - 1, None)
     assert P._lib.STATUS[st] == "PSA_ERR_WORKSPACE_TOO_SMALL"
-    st = L.psa_plan_upload(plan.handle, C.addressof(host), ws_bytes - 1, None)
+    st = L.psa_plan_upload(plan.handle, C.addressof(host), plan.info()["image_bytes"] - 1, None)
     assert P._lib.STATUS[st] == "PSA_ERR_WORKSPACE_TOO_SMALL"
     st = L.psa_decode_attention(plan.handle, C.addressof(host), C.addressof(host), C.addressof(host),
                                 C.addressof(host), None, None, C.addressof(host), ws_bytes, None)
