@@ -148,6 +148,8 @@ typedef struct {
   double distinct_kv_bytes;  /* distinct KV bytes */
   size_t image_bytes;        /* leading part of the workspace that psa_plan_upload fills (the
                                 plan image); what psa_decode_attention_noalloc needs */
+  double unique_kv_bytes;    /* KV bytes over distinct (page, slot) places: a page named by several
+                                groups' prefixes (e.g. the shared root of a flattened tree) once */
 } psa_plan_info;
 
 typedef struct psa_plan psa_plan;

@@ -66,7 +66,7 @@ class psa_plan_info(C.Structure):
                 ("num_matvec_items", C.c_int64), ("num_partial_slots", C.c_int64), ("logical_tokens", C.c_int64),
                 ("processed_tokens", C.c_int64), ("saved_tokens", C.c_int64), ("algorithmic_bytes", C.c_double),
                 ("algorithmic_flops", C.c_double), ("prefix_flops", C.c_double), ("prefix_kv_bytes", C.c_double),
-                ("distinct_kv_bytes", C.c_double), ("image_bytes", C.c_size_t)]
+                ("distinct_kv_bytes", C.c_double), ("image_bytes", C.c_size_t), ("unique_kv_bytes", C.c_double)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -586,6 +586,27 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
                            (double)N * c.num_q_heads * d * (c.out_dtype == PSA_BF16 ? 2 : 4);
   info.algorithmic_flops = 4.0 * d * c.num_q_heads * (double)logical;
   info.prefix_flops = 4.0 * d * c.num_q_heads * (double)prefix_logical;
+  // KV tokens in distinct (page, slot) places: a page named by several groups'
+  // prefixes (the shared root of a flattened tree) counts once, with the most
+  // slots any of them uses.
+  {
+    std::vector<std::pair<int32_t, int32_t>> use;  // (page id, slots used)
+    use.reserve((size_t)(n_gpages + n_qpages));
+    auto mark = [&](const int32_t* pages, int64_t off, int64_t len) {
+      for (int64_t t = 0; t < len; t += P) use.emplace_back(pages[off + t / P], (int32_t)std::min<int64_t>(P, len - t));
+    };
+    for (int g = 0; g < G; ++g) {
+      int64_t vis = 0;
+      for (int t = member_off[g]; t < member_off[g + 1]; ++t) vis = std::max(vis, visible(members[t]));
+      mark(b->group_pages, b->group_page_off[g], vis);
+    }
+    for (int i = 0; i < N; ++i) mark(b->query_pages, b->query_page_off[i], b->query_distinct_len[i]);
+    std::sort(use.begin(), use.end());
+    int64_t unique_tok = 0;
+    for (size_t t = 0; t < use.size(); ++t)
+      if (t + 1 == use.size() || use[t + 1].first != use[t].first) unique_tok += use[t].second;  // max per page
+    info.unique_kv_bytes = (double)unique_tok * tok_bytes;
+  }
   info.image_bytes = (size_t)L.meta_bytes;
 
   plan->items = std::move(items);

@@ -380,6 +380,31 @@ def test_flatten_two_level_workload_keeps_every_context():
         assert flat == [int(x) for x in pages[: -(-n // 16)]]
 
 
+def test_unique_kv_bytes_count_shared_pages_once():
+    """plan_info.unique_kv_bytes: KV over distinct (page, slot) places.  On the
+    flattened two-level workload the 4 root prefixes (1024 tokens) count once,
+    not once per sub-group: 4 * 1024 + 64 * 2048 tokens plus every distinct
+    part; with no shared pages (8x100) it equals prefix + distinct KV bytes;
+    a page two segments share counts the slots of the longer one."""
+    from workloads import make_workload
+
+    wl = make_workload("two_level_4x16x16")
+    batch, _ = P.psa_flatten_prefix_tree(wl.tree)
+    info = P.psa_build_plan(P.make_config(32, 8, 128, wl.num_pages, "bf16"), batch).info()
+    tok = 4 * 1024 + 64 * 2048 + int(np.sum(batch["query_distinct_len"]))
+    assert info["unique_kv_bytes"] == tok * 8 * 128 * 2 * 2
+    assert info["prefix_kv_bytes"] == 64 * 3072 * 8 * 128 * 2 * 2
+    wl = make_workload("llama3_8b_8x100")
+    info = P.psa_build_plan(P.make_config(32, 8, 128, wl.num_pages, "bf16"), wl.batch).info()
+    assert info["unique_kv_bytes"] == info["prefix_kv_bytes"] + info["distinct_kv_bytes"]
+    # two groups naming the same two pages, with 20 and 30 tokens: 30 tokens once; a query of 5 tokens
+    batch = {"page_size": 16, "group_prefix_len": [20, 30], "group_page_off": [0, 2, 4], "group_pages": [3, 4, 3, 4],
+             "query_group": [0, 0, 1, 1, -1], "query_distinct_len": [0, 0, 0, 0, 5],
+             "query_page_off": [0, 0, 0, 0, 0, 1], "query_pages": [7]}
+    info = P.psa_build_plan(P.make_config(4, 2, 64, 8, "bf16"), batch).info()
+    assert info["unique_kv_bytes"] == (30 + 5) * 2 * 64 * 2 * 2
+
+
 def test_flatten_error_paths():
     t = _random_tree(3)
     assert _status(lambda: P.psa_flatten_prefix_tree(dict(t, node_len=[x + 1 for x in t["node_len"]]))) == \
