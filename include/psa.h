@@ -117,8 +117,8 @@ typedef struct {
 #define PSA_PLAN_DEBUG_POISON 0x8u  /* psa_plan_upload fills partial slots with NaN */
 #define PSA_PLAN_NO_XCD_ORDER 0x10u /* plain longest-first order, no XCD grouping */
 #define PSA_PLAN_NO_TILE_PAIRS 0x20u /* MFMA prefix tiles lead each XCD queue (no pairs, no spreading) */
-#define PSA_PLAN_NO_PAGE_SHARING 0x40u /* no family tiles: consecutive groups whose prefixes begin with
-                                          the same pages each cover those pages themselves */
+#define PSA_PLAN_NO_PAGE_SHARING 0x40u /* no shared-page tiles: groups whose prefixes begin with the
+                                          same pages each cover those pages themselves */
 
 /* Plan options; pass NULL for defaults.  Zero fields take defaults. */
 typedef struct {
@@ -157,12 +157,13 @@ typedef struct psa_plan psa_plan;
 /* Validate `batch` against `cfg`, split every KV range into chunks, classify
  * them into MFMA prefix tiles and mat-vec tiles, order the work list (longest
  * first, tiles sharing a prefix chunk on the same XCD) and lay out the
- * workspace.  Consecutively numbered groups whose prefixes begin with the
- * same page ids (at least 64 tokens; psa_flatten_prefix_tree numbers the
- * groups below one shared node this way) form a family: the pages they share
- * are covered once, by MFMA tiles over all the family's requests, unless
- * PSA_PLAN_NO_PAGE_SHARING is set.  Host only; copies everything it needs.  *out receives a new plan
- * on PSA_OK (free with psa_destroy_plan). */
+ * workspace.  Groups whose prefixes begin with the same page ids (whatever
+ * their numbering; psa_flatten_prefix_tree produces such groups from the
+ * nodes above them) share those pages: every run of groups with a common
+ * leading part of at least 64 tokens beyond an enclosing run's covers it
+ * once, with MFMA tiles over all the run's requests, nested to any depth,
+ * unless PSA_PLAN_NO_PAGE_SHARING is set.  Host only; copies everything it
+ * needs.  *out receives a new plan on PSA_OK (free with psa_destroy_plan). */
 psa_status psa_build_plan(const psa_config* cfg, const psa_batch* batch,
                           const psa_plan_opts* opts, psa_plan** out);
 

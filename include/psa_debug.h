@@ -16,12 +16,20 @@ extern "C" {
  * 8 int32 per item = {kind | chunk << 8, kv_head, id, tok_begin, tok_end,
  * page_base, a, b}.  kind 0 = nothing, 1 = mat-vec over query `id`'s pages
  * (page_base indexes group pages followed by query pages; a = partials of the
- * query, b = its partial slot or -1), 2 = MFMA prefix tile of group `id`
- * over rows [a, a + b), rows counted over the plan's whole member array
- * (row = (first member of the group + member) * Hq/Hkv + head in kv group;
- * only as the first item of a unit), 3 = empty partial of query `id`.
+ * query, b = its partial slot or -1), 2 = MFMA prefix tile over group `id`'s
+ * pages for rows [a, a + b) of the plan's member array
+ * (psa_plan_debug_members; the rows may span several groups whose prefixes
+ * hold the same pages there; only as the first item of a unit), 3 = empty
+ * partial of query `id`.
  * capacity_items must be >= 4 * num_items. */
 psa_status psa_plan_debug_items(const psa_plan* plan, int32_t* out, int64_t capacity_items);
+
+/* The plan's member array (MFMA tile rows are counted over it: row = member
+ * index * Hq/Hkv + head in kv group): the queries of every group with members,
+ * in query order within a group; groups whose prefixes begin with the same
+ * pages are adjacent.  *count receives its length; `out` (capacity entries,
+ * may be NULL when capacity is 0) receives the query ids. */
+psa_status psa_plan_debug_members(const psa_plan* plan, int32_t* out, int64_t capacity, int64_t* count);
 
 /* Per query: number of partial results merged into its output (1 = the one
  * tile writes it directly) and its first partial slot (-1 if none). */

@@ -28,7 +28,7 @@ EXPORTS = ["psa_build_plan", "psa_plan_get_info", "psa_plan_upload", "psa_decode
            "psa_last_error", "psa_version", "psa_plan_debug_items", "psa_plan_debug_queries",
            "psa_decode_attention_traced", "psa_debug_read_peak", "psa_debug_mfma_peak",
            "psa_identify_prefix_groups", "psa_prefix_groups_view", "psa_free_prefix_groups",
-           "psa_decode_attention_noalloc"]
+           "psa_decode_attention_noalloc", "psa_plan_debug_members"]
 
 
 class PsaError(RuntimeError):
@@ -117,6 +117,7 @@ def lib():
         L.psa_version.restype = C.c_int32
         L.psa_plan_debug_items.argtypes = [vp, _I32P, C.c_int64]
         L.psa_plan_debug_queries.argtypes = [vp, _I32P, _I32P, C.c_int64]
+        L.psa_plan_debug_members.argtypes = [vp, _I32P, C.c_int64, _I64P]
         L.psa_decode_attention_traced.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp, C.c_int64, vp]
         L.psa_debug_read_peak.argtypes = [vp, C.c_size_t, vp, C.c_int64, vp]
         L.psa_debug_mfma_peak.argtypes = [vp, C.c_int64, C.c_int32, vp]
@@ -198,6 +199,14 @@ class Plan:
         out = np.zeros((max(n, 1), 8), dtype=np.int32)
         _check(lib().psa_plan_debug_items(self.handle, out.ctypes.data_as(_I32P), n))
         return out[:n]
+
+    def members(self):
+        """The member array MFMA tile rows index (psa_debug.h)."""
+        cnt = np.zeros(1, dtype=np.int64)
+        n = self.num_queries  # a query is a member of at most one group
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        _check(lib().psa_plan_debug_members(self.handle, out.ctypes.data_as(_I32P), n, cnt.ctypes.data_as(_I64P)))
+        return out[:int(cnt[0])]
 
     def queries(self):
         """(expected partials, first slot) per query (psa_debug.h)."""

@@ -354,6 +354,15 @@ psa_status psa_plan_debug_items(const psa_plan* plan, int32_t* out, int64_t capa
   return PSA_OK;
 }
 
+psa_status psa_plan_debug_members(const psa_plan* plan, int32_t* out, int64_t capacity, int64_t* count) {
+  if (!plan || !count) return set_error(PSA_ERR_INVALID_ARGUMENT, "NULL plan or count");
+  *count = (int64_t)plan->members.size();
+  if (capacity < *count) return set_error(PSA_ERR_INVALID_ARGUMENT, "capacity too small");
+  if (*count > 0 && !out) return set_error(PSA_ERR_INVALID_ARGUMENT, "NULL output");
+  if (*count > 0) std::memcpy(out, plan->members.data(), plan->members.size() * 4);
+  return PSA_OK;
+}
+
 psa_status psa_plan_debug_queries(const psa_plan* plan, int32_t* expected, int32_t* slot_off, int64_t capacity) {
   if (!plan) return set_error(PSA_ERR_INVALID_ARGUMENT, "NULL plan");
   if (capacity < (int64_t)plan->expected.size()) return set_error(PSA_ERR_INVALID_ARGUMENT, "capacity too small");

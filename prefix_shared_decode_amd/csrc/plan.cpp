@@ -155,17 +155,41 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   const bool bf16 = c.kv_dtype == PSA_BF16;
   const int e = bf16 ? 2 : 4;
 
-  // members of each group, in query order (rows of the MFMA tile)
-  std::vector<int32_t> member_off(G + 1, 0), members;
+  // Sharing of leading prefix pages between groups (BatchLLM summary §4.2:
+  // flattening a multi-level tree gives every group its own copy of the
+  // pages above it).  Groups whose prefixes begin with the same page ids are
+  // made adjacent in the member array (groups sorted by their leading page
+  // ids), so that every set of groups sharing leading pages is one
+  // contiguous run of MFMA rows, whatever their numbering.
+  const bool sharing = use_prefix && bf16 && !limited && !(o.flags & (PSA_PLAN_FORCE_MATVEC | PSA_PLAN_NO_PAGE_SHARING));
+  std::vector<int32_t> nmem(G, 0), gorder(G);
   for (int i = 0; i < N; ++i)
-    if (b->query_group[i] >= 0) ++member_off[b->query_group[i] + 1];
-  for (int g = 0; g < G; ++g) member_off[g + 1] += member_off[g];
-  members.resize(member_off[G]);
+    if (b->query_group[i] >= 0) ++nmem[b->query_group[i]];
+  std::iota(gorder.begin(), gorder.end(), 0);
+  auto whole_pages = [&](int g) { return (int64_t)b->group_prefix_len[g] / P; };
+  auto gpages = [&](int g) { return b->group_pages + b->group_page_off[g]; };
+  if (sharing)
+    std::stable_sort(gorder.begin(), gorder.end(), [&](int x, int y) {
+      const int64_t nx = whole_pages(x), ny = whole_pages(y), n = std::min(nx, ny);
+      const int32_t *px = gpages(x), *py = gpages(y);
+      for (int64_t k = 0; k < n; ++k)
+        if (px[k] != py[k]) return px[k] < py[k];
+      return nx < ny;
+    });
+  // members of each group, in query order, groups in gorder (rows of the MFMA tile)
+  std::vector<int32_t> mstart(G, 0), members;
   {
-    std::vector<int32_t> fill(member_off.begin(), member_off.end() - 1);
+    int64_t cur = 0;
+    for (int g : gorder) {
+      mstart[g] = (int32_t)cur;
+      cur += nmem[g];
+    }
+    members.resize((size_t)cur);
+    std::vector<int32_t> fill(mstart);
     for (int i = 0; i < N; ++i)
       if (b->query_group[i] >= 0) members[fill[b->query_group[i]]++] = i;
   }
+  auto mend = [&](int g) { return mstart[g] + nmem[g]; };
 
   // prefix tiling per group: MFMA tiles (bf16, enough rows) take chunks of
   // up to prefix_chunk_tokens; small groups fall back to per-query mat-vec
@@ -174,61 +198,75 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   std::vector<char> group_mfma(G, 0);
   std::vector<int64_t> group_chunk(G, Cp);
   for (int g = 0; g < G; ++g) {
-    const int64_t rows = (int64_t)(member_off[g + 1] - member_off[g]) * r;
+    const int64_t rows = (int64_t)nmem[g] * r;
     group_mfma[g] = bf16 && !(o.flags & PSA_PLAN_FORCE_MATVEC) && rows >= o.mfma_min_rows;
     if (!group_mfma[g]) group_chunk[g] = std::min<int64_t>(Cp, kMaxMatvecPages * 16);
   }
-  // Families: runs of consecutively numbered groups whose prefixes begin
-  // with the same pages, as a flattened multi-level tree produces for the
-  // sub-groups of one root (BatchLLM summary §4.2: flattening gives each
-  // group its own copy of the shared root).  The tokens [0, S) that a family
-  // shares are covered once, by MFMA tiles whose rows span every member of
-  // the family; each group's own part [S, Lp) is tiled as before.  A family
-  // keeps the length its first two groups share; a later group that shares
-  // less ends it.
-  struct Family {
-    int first, last;  // groups first..last
-    int64_t S;        // shared tokens, whole pages
+  // Shared nodes: over the groups with members, in gorder, the common
+  // leading whole pages of neighbours (lcp) define a tree of intervals (the
+  // LCP-interval tree): the groups of an interval all begin with its shared
+  // length L of tokens.  A node covers the tokens [A, L) its groups share
+  // beyond its nearest covering ancestor (A), once, with MFMA tiles whose
+  // rows span all of its groups' members; a node is kept only if it adds at
+  // least one 64-token block and has enough rows for MFMA tiles (otherwise
+  // its children cover those tokens).  Each group then covers its own
+  // tokens [A_g, Lp) as before, A_g being the level of its deepest node.
+  // Partial indices of a query: its nodes' chunks root first, then its
+  // group's own chunks, then its distinct chunks.
+  struct Node {
+    int lo, hi;      // range of seq (groups with members, in gorder)
+    int64_t A, L;    // tokens [A, L), whole pages
+    int64_t j0;      // partial index of its first chunk
   };
-  std::vector<Family> fams;
-  std::vector<int32_t> fam_of(G, -1);
+  std::vector<Node> nodes;
+  std::vector<int64_t> own_from(G, 0), own_j0(G, 0);
   constexpr int64_t kMinShared = 64;  // at least one 64-token MFMA block
-  if (use_prefix && bf16 && !limited && !(o.flags & (PSA_PLAN_FORCE_MATVEC | PSA_PLAN_NO_PAGE_SHARING))) {
-    auto lead = [&](int g, int h) {  // leading whole pages g and h have in common, in tokens
-      const int64_t n = std::min(b->group_prefix_len[g], b->group_prefix_len[h]) / P;
-      const int32_t* pa = b->group_pages + b->group_page_off[g];
-      const int32_t* pb = b->group_pages + b->group_page_off[h];
-      int64_t k = 0;
-      while (k < n && pa[k] == pb[k]) ++k;
-      return k * P;
-    };
-    auto has_members = [&](int g) { return member_off[g + 1] > member_off[g]; };
-    for (int g = 0; g < G;) {
-      int h = g + 1;
-      int64_t S = 0;
-      if (has_members(g)) {
-        for (; h < G && has_members(h); ++h) {
-          const int64_t sh = lead(g, h);
-          if (h == g + 1) {
-            if (sh < kMinShared) break;
-            S = sh;
-          } else if (sh < S) {
-            break;
-          }
-        }
-      }
-      const int64_t rows = (int64_t)(member_off[h] - member_off[g]) * r;
-      if (h - g >= 2 && rows >= o.mfma_min_rows) {
-        for (int t = g; t < h; ++t) fam_of[t] = (int32_t)fams.size();
-        fams.push_back({g, h - 1, S});
-        g = h;
-      } else {
-        ++g;
-      }
+  if (sharing) {
+    std::vector<int32_t> seq;
+    for (int g : gorder)
+      if (nmem[g] > 0) seq.push_back(g);
+    const int n = (int)seq.size();
+    std::vector<int64_t> lcp(n, 0);  // lcp[k]: leading whole pages (in tokens) seq[k-1] and seq[k] share
+    for (int k = 1; k < n; ++k) {
+      const int64_t m = std::min(whole_pages(seq[k - 1]), whole_pages(seq[k]));
+      const int32_t *pa = gpages(seq[k - 1]), *pb = gpages(seq[k]);
+      int64_t t = 0;
+      while (t < m && pa[t] == pb[t]) ++t;
+      lcp[k] = t * P;
     }
+    struct Range {
+      int lo, hi;
+      int64_t A, j0;
+    };
+    std::vector<Range> todo{{0, n - 1, 0, 0}};
+    while (!todo.empty() && n > 0) {
+      const Range R = todo.back();
+      todo.pop_back();
+      if (R.lo == R.hi) {
+        own_from[seq[R.lo]] = R.A;
+        own_j0[seq[R.lo]] = R.j0;
+        continue;
+      }
+      int64_t m = lcp[R.lo + 1];
+      for (int k = R.lo + 2; k <= R.hi; ++k) m = std::min(m, lcp[k]);
+      const int64_t rows = (int64_t)(mend(seq[R.hi]) - mstart[seq[R.lo]]) * r;
+      int64_t A = R.A, j0 = R.j0;
+      if (m - R.A >= kMinShared && rows >= o.mfma_min_rows) {
+        nodes.push_back({R.lo, R.hi, R.A, m, R.j0});
+        A = m;
+        j0 = R.j0 + ceil_div(m - R.A, Cp);
+      }
+      int start = R.lo;
+      for (int k = R.lo + 1; k <= R.hi; ++k)
+        if (lcp[k] == m) {
+          todo.push_back({start, k - 1, A, j0});
+          start = k;
+        }
+      todo.push_back({start, R.hi, A, j0});
+    }
+    // node tiles read the pages of the run's first group (every group of the run holds them)
+    for (Node& nd : nodes) nd.lo = seq[nd.lo], nd.hi = seq[nd.hi];
   }
-  auto shared_len = [&](int g) { return fam_of[g] >= 0 ? fams[fam_of[g]].S : (int64_t)0; };
-  auto shared_chunks = [&](int g) { return fam_of[g] >= 0 ? ceil_div(fams[fam_of[g]].S, Cp) : (int64_t)0; };
 
   // partial counts per query: prefix chunks first (shared ones, then the
   // group's own), then distinct chunks
@@ -237,9 +275,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   for (int i = 0; i < N; ++i) {
     const int g = b->query_group[i];
     const int64_t lp = visible(i);  // (families form only without limits: lp is the whole prefix there)
-    n_pc[i] = use_prefix && g >= 0
-                  ? (int32_t)(shared_chunks(g) + ceil_div(lp - shared_len(g), group_chunk[g]))
-                  : 0;
+    n_pc[i] = use_prefix && g >= 0 ? (int32_t)(own_j0[g] + ceil_div(lp - own_from[g], group_chunk[g])) : 0;
     const int64_t n_dc = use_distinct ? ceil_div(b->query_distinct_len[i], Cd) : 0;
     expected[i] = n_pc[i] + (int32_t)n_dc;
     if (expected[i] >= 2) {
@@ -258,6 +294,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   struct Cand {
     WorkItem it;
     double cost;
+    bool shared = false;  // MFMA tile of a shared node
   };
   std::vector<Cand> mfma, waves;
   std::vector<int64_t> mfma_set;
@@ -271,7 +308,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   // row counted over the whole member array, so a tile finds its queries
   // without reading a group offset first) for tokens [tb, te) of group g's
   // pages; j = the chunk's partial index for every query of those rows
-  auto mfma_tiles = [&](int g, int64_t row0, int64_t rows, int32_t tb, int32_t te_chunk, int64_t j) {
+  auto mfma_tiles = [&](int g, int64_t row0, int64_t rows, int32_t tb, int32_t te_chunk, int64_t j, bool shared) {
     const int32_t pbase = (int32_t)(b->group_page_off[g] + tb / P);
     const int64_t ntiles = ceil_div(rows, tile_max);
     const int64_t per = round_up(ceil_div(rows, ntiles), 16);
@@ -290,28 +327,27 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
         const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
         WorkItem it{(int32_t)(ITEM_PREFIX_MFMA | (j << 8)), kvh, g, tb, te, pbase, (int32_t)(row0 + rb), (int32_t)rc};
         const double fl = (double)round_up(te - tb, 64) * round_up(rc, 16) * d * 4;
-        mfma.push_back({it, fixed + std::max(fl / mfma_slot, 4.0 * kv_bytes / bw_wave)});
+        mfma.push_back({it, fixed + std::max(fl / mfma_slot, 4.0 * kv_bytes / bw_wave), shared});
         mfma_set.push_back(set);
         ++n_prefix_items;
       }
     }
   };
-  for (size_t f = 0; f < fams.size() && use_prefix; ++f) {  // the families' shared tokens
-    const Family& F = fams[f];
-    const int64_t rows = (int64_t)(member_off[F.last + 1] - member_off[F.first]) * r;
-    for (int64_t ch = 0; ch < ceil_div(F.S, Cp); ++ch)
-      mfma_tiles(F.first, (int64_t)member_off[F.first] * r, rows, (int32_t)(ch * Cp),
-                 (int32_t)std::min(F.S, (ch + 1) * Cp), ch);
+  for (const Node& nd : nodes) {  // shared nodes: tokens [A, L) of every group of the run, once
+    const int64_t rows = (int64_t)(mend(nd.hi) - mstart[nd.lo]) * r;
+    for (int64_t ch = 0; ch < ceil_div(nd.L - nd.A, Cp); ++ch)
+      mfma_tiles(nd.lo, (int64_t)mstart[nd.lo] * r, rows, (int32_t)(nd.A + ch * Cp),
+                 (int32_t)std::min(nd.L, nd.A + (ch + 1) * Cp), nd.j0 + ch, true);
   }
   for (int g = 0; g < G && use_prefix; ++g) {  // each group's own tokens
     int64_t lp = b->group_prefix_len[g];
-    const int nm = member_off[g + 1] - member_off[g];
+    const int nm = nmem[g];
     if (limited) {  // tokens past every member's limit need no tiles
       int64_t vmax = 0;
-      for (int t = member_off[g]; t < member_off[g + 1]; ++t) vmax = std::max(vmax, visible(members[t]));
+      for (int t = mstart[g]; t < mend(g); ++t) vmax = std::max(vmax, visible(members[t]));
       lp = vmax;
     }
-    const int64_t S = shared_len(g), j0 = shared_chunks(g);
+    const int64_t S = own_from[g], j0 = own_j0[g];
     if (lp <= S || nm == 0) continue;
     const int64_t rows = (int64_t)nm * r;
     const bool mf = group_mfma[g];
@@ -321,11 +357,11 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
       const int32_t tb = (int32_t)(S + ch * C), te = (int32_t)std::min(lp, S + (ch + 1) * C);
       const int64_t j = j0 + ch;
       if (mf) {
-        mfma_tiles(g, (int64_t)member_off[g] * r, rows, tb, te, j);
+        mfma_tiles(g, (int64_t)mstart[g] * r, rows, tb, te, j, false);
       } else {
         const int32_t pbase = (int32_t)(b->group_page_off[g] + tb / P);
         const double kv_bytes = (double)round_up(te - tb, P) * d * e * 2;
-        for (int t = member_off[g]; t < member_off[g + 1]; ++t) {
+        for (int t = mstart[g]; t < mend(g); ++t) {
           const int qi = members[t];
           const int64_t vis = visible(qi);
           if (vis <= tb) continue;  // this query's prefix ends before the chunk
@@ -368,17 +404,18 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     WorkItem it[kUnitItems];
     double cost;
     int64_t set;  // units of one set re-read one prefix chunk: same XCD
+    bool shared;  // an MFMA tile of a shared node
   };
   std::vector<Unit> units;
   const WorkItem nop{ITEM_NOP, 0, 0, 0, 0, 0, 0, -1};
   for (size_t t = 0; t < mfma.size(); ++t) {
-    Unit u{{mfma[t].it, nop, nop, nop}, mfma[t].cost, mfma_set[t]};
+    Unit u{{mfma[t].it, nop, nop, nop}, mfma[t].cost, mfma_set[t], mfma[t].shared};
     units.push_back(u);
   }
   std::stable_sort(waves.begin(), waves.end(), [](const Cand& a, const Cand& b2) { return a.cost > b2.cost; });
   int64_t next_set = (int64_t)mfma.size() + 1 + (mfma_set.empty() ? 0 : *std::max_element(mfma_set.begin(), mfma_set.end()));
   for (size_t t = 0; t < waves.size(); t += kUnitItems) {
-    Unit u{{nop, nop, nop, nop}, 0.0, next_set++};
+    Unit u{{nop, nop, nop, nop}, 0.0, next_set++, false};
     for (int w = 0; w < kUnitItems && t + w < waves.size(); ++w) {
       u.it[w] = waves[t + w].it;
       u.cost = std::max(u.cost, waves[t + w].cost);
@@ -427,10 +464,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     // family tiles first instead: they pair with the groups' own, longer
     // tiles on the CUs (flattened 4x16x16 prefix-only: 0.126 ms against
     // 0.140 ms longest first).
-    auto family = [&](int64_t u) {
-      const WorkItem& w = units[u].it[0];
-      return w.kind % 256 == ITEM_PREFIX_MFMA && (int64_t)w.a + w.b > (int64_t)member_off[w.id + 1] * r;
-    };
+    auto family = [&](int64_t u) { return units[u].shared; };
     for (auto& qq : q) {
       const bool tiles_only = std::all_of(qq.begin(), qq.end(), [&](int64_t u) {
         return units[u].it[0].kind % 256 == ITEM_PREFIX_MFMA;
@@ -545,7 +579,8 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   if (!items.empty()) std::memcpy(img.data() + L.items, items.data(), items.size() * sizeof(WorkItem));
   for (int64_t t = 0; t < n_gpages; ++t) put32(L.pages, t, b->group_pages[t]);
   for (int64_t t = 0; t < n_qpages; ++t) put32(L.pages, n_gpages + t, b->query_pages[t]);
-  for (int g = 0; g <= G; ++g) put32(L.member_off, g, member_off[g]);
+  for (int g = 0; g < G; ++g) put32(L.member_off, g, mstart[g]);
+  put32(L.member_off, G, (int64_t)members.size());
   for (size_t t = 0; t < members.size(); ++t) put32(L.members, t, members[t]);
   for (int i = 0; i < N; ++i) {
     put32(L.expected, i, expected[i]);
@@ -565,7 +600,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   info.num_partial_slots = slots * hkv;
   int64_t logical = 0, processed = 0, prefix_logical = 0;
   for (int g = 0; g < G; ++g)
-    if (member_off[g + 1] > member_off[g]) processed += b->group_prefix_len[g];
+    if (nmem[g] > 0) processed += b->group_prefix_len[g];
   for (int i = 0; i < N; ++i) {
     const int64_t lp = visible(i);
     logical += lp + b->query_distinct_len[i];
@@ -577,7 +612,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   info.saved_tokens = logical - processed;
   int64_t prefix_once = 0, distinct_tok = 0;
   for (int g = 0; g < G; ++g)
-    if (member_off[g + 1] > member_off[g]) prefix_once += b->group_prefix_len[g];
+    if (nmem[g] > 0) prefix_once += b->group_prefix_len[g];
   for (int i = 0; i < N; ++i) distinct_tok += b->query_distinct_len[i];
   const double tok_bytes = (double)hkv * d * 2 * e;
   info.prefix_kv_bytes = (double)prefix_once * tok_bytes;
@@ -597,7 +632,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     };
     for (int g = 0; g < G; ++g) {
       int64_t vis = 0;
-      for (int t = member_off[g]; t < member_off[g + 1]; ++t) vis = std::max(vis, visible(members[t]));
+      for (int t = mstart[g]; t < mend(g); ++t) vis = std::max(vis, visible(members[t]));
       mark(b->group_pages, b->group_page_off[g], vis);
     }
     for (int i = 0; i < N; ++i) mark(b->query_pages, b->query_page_off[i], b->query_distinct_len[i]);
@@ -609,6 +644,7 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
   }
   info.image_bytes = (size_t)L.meta_bytes;
 
+  plan->members = members;
   plan->items = std::move(items);
   plan->expected = std::move(expected);
   plan->slot_off = std::move(slot_off);

@@ -18,6 +18,7 @@ struct psa_plan {
   psa::ImageLayout layout{};
   std::vector<uint8_t> image;          // bytes [0, layout.meta_bytes) of the workspace
   std::vector<psa::WorkItem> items;    // host copy of the work list (tests), 4 per unit
+  std::vector<int32_t> members;        // member array: the queries of each group, groups in sharing order
   int64_t num_units = 0;               // workgroups of the fused launch
   int64_t num_group_pages = 0;         // query pages follow the group pages in the page array
   uint32_t part_o_bytes = 0, part_ml_bytes = 0;

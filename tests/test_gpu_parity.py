@@ -191,6 +191,47 @@ def test_random_prefix_limits(seed):
 
 # ---------------- edge cases ----------------
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_shared_nodes_with_scattered_group_numbers(seed):
+    """A flattened two-level tree whose groups are renumbered at random: the
+    groups of one root are no longer consecutive, the plan still shares the
+    root's tokens across them; the output equals the oracle's (contexts read
+    from the tree), and the plan without page sharing's."""
+    from workloads import permute_groups
+
+    wl = build_two_level("two_level_perm", 32, 8, 128, "bf16", 3, 128, 4, 96, 5, (0, 70), seed=40 + seed)
+    batch, _ = P.psa_flatten_prefix_tree(wl.tree)
+    batch = permute_groups(batch, np.random.default_rng(seed).permutation(len(batch["group_prefix_len"])))
+    q, k, v = values(wl)
+    O, M, L = oracle.decode_attention(to_host64(q), to_host64(k), to_host64(v),
+                                      oracle.flatten_tree(wl.tree, [-1] * len(wl.tree["query_node"])))
+    for kw in ({}, {"prefix_chunk_tokens": 64, "mfma_tile_rows": 32}, {"flags": P.NO_PAGE_SHARING}):
+        log(f"case scattered groups seed {seed} {kw}")
+        _, out, m, l = run(wl, batch, q, k, v, **kw)
+        assert_close(to_host64(out), O, "bf16", f"scattered groups {kw}")
+        assert_lse_close(m, l, M, L, 2e-4)
+
+
+@pytest.mark.parametrize("r", [1, 4])
+def test_nested_shared_nodes(r):
+    """Three-level tree (roots 512, children 256, leaves 128, 8 requests per
+    leaf), flattened to leaf groups: root and middle tokens are each tiled
+    once over all the groups below them (nested shared nodes).  Output equals
+    the oracle's, read from the tree, with default and small chunks."""
+    from workloads import build_tree
+
+    wl = build_tree("nested", 8 * r, 8, 128, "bf16", [(2, 512), (2, 256), (2, 128)], 8, (0, 50), seed=7 + r)
+    batch, _ = P.psa_flatten_prefix_tree(wl.tree)
+    q, k, v = values(wl)
+    O, M, L = oracle.decode_attention(to_host64(q), to_host64(k), to_host64(v),
+                                      oracle.flatten_tree(wl.tree, [-1] * len(wl.tree["query_node"])))
+    for kw in ({}, {"prefix_chunk_tokens": 128, "distinct_chunk_tokens": 32}):
+        log(f"case nested r {r} {kw}")
+        _, out, m, l = run(wl, batch, q, k, v, **kw)
+        assert_close(to_host64(out), O, "bf16", f"nested r {r} {kw}")
+        assert_lse_close(m, l, M, L, 2e-4)
+
+
 def test_stale_padding_is_masked():
     wl = build_single_level("stale", 32, 8, 128, "bf16", [(37, 17, (0, 35))], (3, (1, 20)), seed=3)
     q, k, v = values(wl)

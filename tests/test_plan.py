@@ -61,7 +61,15 @@ def _coverage(wl, plan):
     for i, g in enumerate(b["query_group"]):
         if g >= 0:
             members.setdefault(int(g), []).append(i)
-    member_list = [i for g in sorted(members) for i in members[g]]  # the plan's member array
+    member_list = [int(x) for x in plan.members()]  # the plan's member array
+    # it lists each group's members in query order, every group with members once, contiguously
+    assert sorted(member_list) == sorted(i for g in members for i in members[g])
+    first_row = {}
+    for mi, qi in enumerate(member_list):
+        g = int(b["query_group"][qi])
+        first_row.setdefault(g, mi)
+    for g, qs in members.items():
+        assert member_list[first_row[g]: first_row[g] + len(qs)] == qs
     lim = b.get("query_prefix_len")
     items = plan.items()
     assert len(items) % 4 == 0
@@ -85,10 +93,8 @@ def _coverage(wl, plan):
         elif kind == 2:
             assert a % r == 0 and bb % r == 0 and 0 < bb <= 128
             assert pbase == b["group_page_off"][ident] + tb // 16
-            first = sum(len(members.get(g2, [])) for g2 in range(ident))  # the group's first member, over all groups
-            assert first * r <= a
-            # rows past the group's own members belong to the following groups,
-            # which must hold the same pages for these tokens (a family tile)
+            # rows of other groups than `ident` (a shared-node tile) must hold
+            # the same pages for these tokens
             own = b["group_pages"][b["group_page_off"][ident] + tb // 16: b["group_page_off"][ident] + (te + 15) // 16]
             for mi in range(a // r, (a + bb) // r):
                 qi = member_list[mi]
@@ -97,7 +103,7 @@ def _coverage(wl, plan):
                     continue  # this row's prefix limit ends before the tile: no piece
                 g2 = int(b["query_group"][qi])
                 if g2 != ident:
-                    assert g2 > ident and te <= b["group_prefix_len"][g2]
+                    assert te <= b["group_prefix_len"][g2]
                     other = b["group_pages"][b["group_page_off"][g2] + tb // 16: b["group_page_off"][g2] + (te + 15) // 16]
                     assert list(other) == list(own), (ident, g2, tb, te)
                 cov.setdefault((qi, kvh), []).append(("p", tb, te if vis is None else min(te, vis),
@@ -510,6 +516,62 @@ def test_family_tiles_cover_a_shared_root_once():
 
 
 @pytest.mark.parametrize("seed", range(3))
+def test_shared_nodes_do_not_need_consecutive_group_numbers(seed):
+    """The flattened 4x16x16 batch with its 64 groups renumbered at random (a
+    root's 16 groups scattered over the numbering): the plan still tiles each
+    root's 1024 tokens once over all of its members (the same 768 MFMA tiles,
+    3 pieces per query), and covers every token once."""
+    from workloads import make_workload, permute_groups
+
+    fw = _flat(make_workload("two_level_4x16x16"))
+    perm = np.random.default_rng(seed).permutation(len(fw.batch["group_prefix_len"]))
+    fw.batch = permute_groups(fw.batch, perm)
+    plan = P.psa_build_plan(_cfg(fw), fw.batch)
+    it = plan.items()
+    mf = it[(it[:, 0] & 0xFF) == 2]
+    assert len(mf) == 768
+    assert len(mf[mf[:, 4] == 1024]) == 256 and (mf[mf[:, 4] == 1024][:, 7] == 128).all()
+    expected, _ = plan.queries()
+    assert (expected == 3).all()
+    _check_coverage(fw, plan)
+
+
+@pytest.mark.parametrize("r", [1, 4])
+def test_nested_shared_nodes_three_levels(r):
+    """A three-level tree (2 roots of 512 tokens, 2 children of 256 each, 2
+    leaves of 128 each, 8 requests per leaf) flattens to 8 leaf groups of 896
+    tokens.  The plan covers each root's 512 tokens once over its 4 groups,
+    each middle node's 256 tokens once over its 2 groups, and each group's
+    own 128 tokens (MFMA tiles at r 4, mat-vec at r 1, below 16 rows): at r
+    4 per kv head 2 + 4 + 8 tiles, and 3 prefix pieces per query.  Without page sharing, 8 tiles per
+    kv head over 896 tokens."""
+    from workloads import build_tree
+
+    wl = build_tree("t3", 4 * r, 4, 64, "bf16", [(2, 512), (2, 256), (2, 128)], 8, (1, 40), seed=3)
+    fw = _flat(wl)
+    assert set(fw.batch["group_prefix_len"].tolist()) == {896}
+    plan = P.psa_build_plan(_cfg(fw), fw.batch)
+    it = plan.items()
+    mf = it[((it[:, 0] & 0xFF) == 2) & (it[:, 1] == 0)]
+    spans = sorted(set((int(a), int(b)) for a, b in mf[:, 3:5]))
+    own_mfma = 8 * r >= 16  # a group's own rows (at r 1 its own tokens go to mat-vec tiles)
+    assert spans == [(0, 512), (512, 768)] + ([(768, 896)] if own_mfma else [])
+    rows = {sp: int(mf[(mf[:, 3] == sp[0]) & (mf[:, 4] == sp[1])][:, 7].sum()) for sp in spans}
+    assert rows == {sp: 64 * r for sp in spans}
+    if r == 4:
+        assert len(mf) == 2 + 4 + 8
+    expected, _ = plan.queries()
+    dl = np.asarray(fw.batch["query_distinct_len"])
+    assert (expected == 3 + (dl > 0)).all()
+    _check_coverage(fw, plan)
+    plain = P.psa_build_plan(_cfg(fw), fw.batch, flags=P.NO_PAGE_SHARING)
+    pm = plain.items()
+    pm = pm[((pm[:, 0] & 0xFF) == 2) & (pm[:, 1] == 0)]
+    assert sorted(set((int(a), int(b)) for a, b in pm[:, 3:5])) == ([(0, 896)] if own_mfma else [])
+    _check_coverage(fw, plain)
+
+
+@pytest.mark.parametrize("seed", range(3))
 @pytest.mark.parametrize("r", [1, 4, 8])
 def test_family_tiles_edge_shapes(seed, r):
     """Family tiles next to empty and mat-vec own parts, several chunks of the
@@ -522,7 +584,7 @@ def test_family_tiles_edge_shapes(seed, r):
     it = plan.items()
     mf = it[(it[:, 0] & 0xFF) == 2]
     rows = (3 + 2 + 1 + 1) * r  # the family's members
-    fam = mf[(mf[:, 2] == 0) & (mf[:, 4] <= 64)]
+    fam = mf[np.isin(mf[:, 2], [0, 1, 2, 3]) & (mf[:, 4] <= 64)]  # tiles may read any family group's pages
     if rows >= 16:
         assert len(fam) > 0 and fam[fam[:, 1] == 0][:, 7].sum() == rows
     for kw in ({}, {"prefix_chunk_tokens": 32}, {"prefix_chunk_tokens": 48, "mfma_tile_rows": 16},

@@ -10,6 +10,8 @@ from .synth import (  # noqa: F401
     make_workload,
     build_single_level,
     build_two_level,
+    build_tree,
+    permute_groups,
     share_leading_pages,
     build_family_case,
     build_token_batch,

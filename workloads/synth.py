@@ -207,6 +207,68 @@ def build_two_level(name, hq, hkv, d, dtype, n_roots, root_len, n_subs, sub_len,
     return wl
 
 
+def build_tree(name, hq, hkv, d, dtype, levels, n_req, dist_range, seed=0, P=PAGE):
+    """Prefix tree of any depth: ``levels`` = [(branching, tokens), ...] from
+    the roots down (level 0 has ``branching`` roots; every node of level k has
+    ``branching_{k+1}`` children); ``n_req`` requests hang under each node of
+    the last level, each with its own distinct tokens drawn from
+    ``dist_range``.  Node lengths must be page multiples.  Like
+    ``build_two_level``, ``batch`` is left empty until flattened."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    node_parent, node_len, frontier = [], [], [-1]
+    for branching, tokens in levels:
+        nxt = []
+        for parent in frontier:
+            for _ in range(branching):
+                nxt.append(len(node_parent))
+                node_parent.append(parent)
+                node_len.append(int(tokens))
+        frontier = nxt
+    query_node = [leaf for leaf in frontier for _ in range(n_req)]
+    lo, hi = dist_range
+    dlen = [int(x) for x in rng.integers(lo, hi, size=len(query_node), endpoint=True)]
+    need = sum(-(-x // P) for x in node_len) + sum(-(-x // P) for x in dlen)
+    perm = rng.permutation(need)
+    noff, npages, used = _alloc(perm, node_len, P)
+    qoff, qpages, _ = _alloc(perm[used:], dlen, P)
+    tree = {
+        "page_size": P,
+        "node_parent": np.asarray(node_parent, dtype=np.int32),
+        "node_len": np.asarray(node_len, dtype=np.int32),
+        "node_page_off": noff,
+        "node_pages": npages,
+        "query_node": np.asarray(query_node, dtype=np.int32),
+        "query_distinct_len": np.asarray(dlen, dtype=np.int32),
+        "query_page_off": qoff,
+        "query_pages": qpages,
+    }
+    return Workload(name, hq, hkv, d, dtype, need, {}, tree, seed, P)
+
+
+def permute_groups(batch, perm):
+    """The same batch with group g renumbered perm[g] (page tables moved with
+    it); queries keep their order.  Groups that share leading pages are then
+    no longer numbered consecutively."""
+    perm = np.asarray(perm, dtype=np.int64)
+    G = len(batch["group_prefix_len"])
+    inv = np.empty(G, dtype=np.int64)
+    inv[perm] = np.arange(G)
+    lens, pages, off = [], [], [0]
+    for new in range(G):
+        g = int(inv[new])
+        a, b = int(batch["group_page_off"][g]), int(batch["group_page_off"][g + 1])
+        lens.append(int(batch["group_prefix_len"][g]))
+        pages.extend(int(x) for x in batch["group_pages"][a:b])
+        off.append(len(pages))
+    out = dict(batch)
+    out["group_prefix_len"] = np.asarray(lens, dtype=np.int32)
+    out["group_page_off"] = np.asarray(off, dtype=np.int64)
+    out["group_pages"] = np.asarray(pages, dtype=np.int32)
+    qg = np.asarray(batch["query_group"], dtype=np.int64)
+    out["query_group"] = np.where(qg >= 0, perm[np.maximum(qg, 0)], -1).astype(np.int32)
+    return out
+
+
 def _mixed(seed):
     return build_mixed("mixed_7prefill_256decode", 32, 8, 128, "bf16", [(2048, 128, (64, 512))] * 2,
                        [(1024, 512)] * 7, seed)
