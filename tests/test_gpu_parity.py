@@ -476,17 +476,19 @@ def test_measured_peak_kernels_run():
     # bytes of value 1: the xor of an even number of 16-byte chunks per thread
     assert int((sink == -1).sum()) == 0
     assert bool(torch.isfinite(out).all())
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    P.psa_debug_read_peak(buf, sink)
-    b.record()
-    b.synchronize()
-    assert buf.numel() / (a.elapsed_time(b) / 1e3) > 1e12
-    a.record()
-    P.psa_debug_mfma_peak(out, 1024)
-    b.record()
-    b.synchronize()
-    assert flops * 4 / (a.elapsed_time(b) / 1e3) > 5e14
+    def best_ms(fn, reps=5):  # one launch can be slowed by clocks ramping or a neighbour: take the best
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return min(ts)
+
+    assert buf.numel() / (best_ms(lambda: P.psa_debug_read_peak(buf, sink)) / 1e3) > 1e12
+    assert flops * 4 / (best_ms(lambda: P.psa_debug_mfma_peak(out, 1024)) / 1e3) > 5e14
 
 
 
