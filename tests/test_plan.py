@@ -356,6 +356,37 @@ def test_flatten_matches_oracle_optimum(seed):
         assert flat == pages[: -(-n // 16)]
 
 
+@pytest.mark.parametrize("seed", range(30))
+def test_flatten_matches_brute_force_directly(seed):
+    """The C++ flattening's saving equals the best over every set partition
+    of the queries (a block saves its deepest common node's path length times
+    its size minus one), computed by brute force, not through the oracle's
+    dynamic program."""
+    from test_oracle_flatten import brute_force
+
+    t = _random_tree(1000 + seed)
+    _, saved = P.psa_flatten_prefix_tree(t)
+    assert saved == brute_force(t["node_parent"], t["node_len"], t["query_node"])
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_identification_matches_brute_force_directly(seed):
+    """psa_identify_prefix_groups on small random token sets (duplicates and
+    prompts that are prefixes of others included) saves exactly the best over
+    every set partition, each block saving its longest common prefix times its
+    size minus one (brute force, not the oracle's trie and DP)."""
+    from test_oracle_flatten import brute_force_tokens
+
+    rng = np.random.default_rng(2000 + seed)
+    n = int(rng.integers(1, 8))
+    seqs = [[int(x) for x in rng.integers(0, int(rng.integers(1, 4)), size=int(rng.integers(0, 7)))] for _ in range(n)]
+    if n >= 3 and rng.random() < 0.4:
+        seqs[1] = list(seqs[0])
+        seqs[2] = list(seqs[0][: len(seqs[0]) // 2])
+    res = P.psa_identify_prefix_groups(seqs)
+    assert res["saved_tokens"] == brute_force_tokens(seqs)
+
+
 def test_flatten_two_level_workload_closed_form():
     wl = build_two_level("t", 32, 8, 128, "bf16", 4, 1024, 16, 2048, 16, (32, 256))
     batch, saved = P.psa_flatten_prefix_tree(wl.tree)
