@@ -424,6 +424,8 @@ def run_one(args):
     kv_alg = info["prefix_kv_bytes"] + info["distinct_kv_bytes"]
     bytes_single_level = info["algorithmic_bytes"]
     bytes_alg = bytes_single_level - kv_alg + info["unique_kv_bytes"]
+    if args.flags & P.DISTINCT_ONLY:  # a distinct-only plan streams the distinct KV, q and out
+        bytes_alg = bytes_single_level - info["prefix_kv_bytes"]
     achieved = bytes_alg / sec / 1e9
     traffic = load_traffic(wl.name, bytes_alg)
     rec = {
@@ -464,10 +466,18 @@ def run_one(args):
     }
     if info["prefix_flops"] > 0:
         rec["roofline"]["prefix_flops_per_launch"] = info["prefix_flops"]
+    if args.flags & P.PREFIX_ONLY:  # the prefix tiles alone: matrix-core bound
+        tf = info["prefix_flops"] / sec / 1e12
+        rec["roofline"].update({"bound": "mfma", "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": tf / BF16_MFMA_PEAK_TFLOPS})
+        rec["hbm_roofline_frac"] = None
     if not args.no_peaks and flush is not None:
         rec["measured_peaks"] = measured_peaks(P, flush, max(5, args.steps // 5))
         mp = rec["measured_peaks"]
-        rec["roofline"]["frac_of_measured_read_peak"] = achieved / mp["hbm_read_GBps"]
+        if args.flags & P.PREFIX_ONLY:
+            rec["roofline"]["frac_of_measured_mfma_peak"] = rec["roofline"]["achieved"] / mp["mfma_bf16_TFLOPs"]
+        else:
+            rec["roofline"]["frac_of_measured_read_peak"] = achieved / mp["hbm_read_GBps"]
     if not args.no_components and args.flags == 0 and info["num_prefix_items"] > 0:
         rec["components"] = components(P, cfg, batch, wl, q, k, v, flush, sink, max(10, args.steps // 2), ms,
                                        rec.get("measured_peaks"))
