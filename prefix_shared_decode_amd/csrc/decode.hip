@@ -752,12 +752,12 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
   if (valid < 64 || limits) {  // last block of the chunk, or rows with their own limits
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
-      const int lim = min(valid, limb[sl]);
+      const int lim = min(valid, limb[sl]) - 8 * lg;  // against the token's offset from 8 lg
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if ((t >> 1) * 32 + 8 * lg + 4 * (t & 1) + i >= lim) s[sl][t][i] = -INFINITY;
+          if ((t >> 1) * 32 + 4 * (t & 1) + i >= lim) s[sl][t][i] = -INFINITY;
     }
   }
   // ---- online softmax per row (lane's row = l16; 16 raw scores per lane) ----
@@ -1252,10 +1252,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lds1[Lds<D, R, BF16>::MF];
   const uint64_t t0 = p.trace ? __builtin_amdgcn_s_memrealtime() : 0;
   const WorkItem* unit = p.items + (int64_t)blockIdx.x * kUnitItems;
-  // the image header and this unit's first word load together (scalar loads, one wait)
+  // The image header, the unit's first word and this wave's item load
+  // together (one wait): a mat-vec wave then starts its page table and q
+  // loads one round trip earlier.  (The unit lies inside the image the host
+  // checked; nothing loaded is used before the header is.)
   const uint64_t hdr = *reinterpret_cast<const uint64_t*>(p.header);
   const int word0 = unit[0].kind;
-  asm volatile("" ::"s"(hdr), "s"(word0));
+  const WorkItem it = unit[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
+  asm volatile("" ::"s"(hdr), "s"(word0), "s"(it.kind), "s"(it.tok_end), "s"(it.b));
   if (hdr != (((uint64_t)p.plan_id << 32) | kImageMagic)) {
     poison_outputs<D>(p);
     return;
@@ -1265,7 +1269,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams p) {
     if constexpr (BF16)
       prefix_mfma_tile<D, R>(p, unit[0], (lds_char*)lds0, (lds_char*)lds1);
   } else {
-    const WorkItem it = unit[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
     const int kind = it.kind & 0xff;
     if (kind == ITEM_MATVEC)
       matvec_wave<D, R, BF16>(p, it, lds0);
