@@ -114,7 +114,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 #ifndef PSA_MV_PAGES
 #define PSA_MV_PAGES 2
 #endif
-constexpr int kMvPages = PSA_MV_PAGES;  // mat-vec tile: pages of K and V in flight per wave
+constexpr int kMvPages = PSA_MV_PAGES;  // mat-vec tile: bf16 pages of K and V in flight per wave
+// (an fp32 page is twice the bytes: two of them with d 128 and R 8 do not fit
+// the register budget, so that shape keeps one page in flight)
+template <int D, int R, bool BF16>
+constexpr int mv_pages() { return BF16 || D * R < 1024 ? kMvPages : 1; }
 constexpr int kMergeUnroll = 4;         // in-register merges of up to this many pieces load in one pass
 constexpr int kSc1 = 16;  // cache policy: coherent at device (agent) scope
 constexpr int kNt = 2;    // cache policy: non-temporal (streamed once; keeps reused prefix K/V and
@@ -398,20 +402,21 @@ __device__ __forceinline__ void matvec_wave(const DecodeParams& p, const WorkIte
       for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
     }
     bool over = false;
-    // a ring of kMvPages page buffers: page j lives in buffer j % kMvPages,
-    // and its load is issued kMvPages pages ahead of its use
-    PageRegs<D, R, BF16> b[kMvPages];
+    // a ring of NP page buffers: page j lives in buffer j % NP, and its load
+    // is issued NP pages ahead of its use
+    constexpr int NP = mv_pages<D, R, BF16>();
+    PageRegs<D, R, BF16> b[NP];
 #pragma unroll
-    for (int u = 0; u < kMvPages; ++u) load(b[u], u);
+    for (int u = 0; u < NP; ++u) load(b[u], u);
     page(b[0], 0, !fixed_ref, over);
-    load(b[0], kMvPages);
-    for (int j = 1; j < npages; j += kMvPages) {
-      if (!ctr_read && j + kMvPages >= npages) read_ctr();
+    load(b[0], NP);
+    for (int j = 1; j < npages; j += NP) {
+      if (!ctr_read && j + NP >= npages) read_ctr();
 #pragma unroll
-      for (int u = 0; u < kMvPages; ++u) {
-        const int bi = (u + 1) % kMvPages;
+      for (int u = 0; u < NP; ++u) {
+        const int bi = (u + 1) % NP;
         if (j + u < npages) page(b[bi], j + u, false, over);  // wave-uniform; loads past the end read zeros
-        load(b[bi], j + u + kMvPages);
+        load(b[bi], j + u + NP);
       }
     }
     if (!ctr_read) read_ctr();

@@ -1,4 +1,4 @@
-"""Register budget of the fused kernel: no bf16 instantiation uses scratch.
+"""Register budget of the fused kernel: no instantiation uses scratch.
 
 The compiler's resource remarks for decode.hip, built with the library's
 own flags for gfx950 (host cross-compile, no GPU needed).  A spill or a
@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 @pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not installed")
-def test_bf16_instantiations_use_no_scratch(tmp_path):
+def test_no_instantiation_uses_scratch(tmp_path):
     from prefix_shared_decode_amd.build import ARCH, COMMON
 
     src = os.path.join(ROOT, "prefix_shared_decode_amd", "csrc", "decode.hip")
@@ -31,6 +31,5 @@ def test_bf16_instantiations_use_no_scratch(tmp_path):
     assert len(names) == len(scratch) == 16, (names, scratch)
     usage = dict(zip(names, scratch))
     # decode_kernel<D, R, BF16>: mangled ...ILi<D>ELi<R>ELb<0|1>E...
-    bf16 = {n: s for n, s in usage.items() if re.search(r"ELb1E", n)}
-    assert len(bf16) == 8
-    assert all(s == 0 for s in bf16.values()), bf16
+    assert len([n for n in usage if re.search(r"ELb1E", n)]) == 8
+    assert all(s == 0 for s in usage.values()), usage
