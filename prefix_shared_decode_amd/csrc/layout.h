@@ -36,15 +36,27 @@ struct MfLayout {
 };
 
 // chunk XOR key of token t (t within a 64-token block).  Any key that is a
-// function of the token keeps the copy and the reads consistent; this one
-// (token bits 0, 1, 3, 4 for D 128; 0, 1, 3 for D 64) was chosen by timing
-// every key made of token bits on gfx950: with it the K operand reads
-// (ds_read_b128) and the transposing V reads run at the rate of
-// conflict-free linear reads, while e.g. the same bits in the order
-// 4, 3, 0, 1 make the K reads 1.55x slower.
+// function of the token keeps the copy and the reads consistent; these were
+// chosen by timing keys made of token bits on gfx950, two workgroups per CU
+// (where the LDS, not the issue, bounds the reads):
+// - D 128: token bits 0, 1, 3 in key bits 1, 2, 3 (key bit 0 stays 0).  A
+//   K operand read (ds_read_b128) is served 8 lanes at a time, whose 8
+//   tokens differ in bits 0, 1, 3: their chunks must differ.  A transposing
+//   V read (ds_read_b64_tr_b16) is served 32 lanes at a time: 8 tokens (bits
+//   0, 1, 3 again) x the two chunks 2nb and 2nb + 1, which fill all 64
+//   banks only if key bit 0 is the same for all 8 tokens.  The previous key
+//   (bits 0, 1, 3, 4 in key bits 0..3) made every V read take two passes
+//   (the bank-conflict counter's half of the V reads' LDS cycles; 26.9
+//   against 18.3 cycles per read and wave), and e.g. bits 4, 2, 0, 1 make
+//   the K reads 1.8x slower.
+// - D 64 (rows of 128 bytes, two tokens per bank line, token bit 0 picks
+//   the line's half): token bits 0, 1, 3.
+// The key of a read's token depends only on the lane (bits 0, 1 and 3 of the
+// token come from the lane, bits 2 and 5 from the read's step), so a read is
+// a per-lane base plus a step the kernel adds as an immediate.
 template <int D>
 PSA_HD int kswz(int t) {
-  if (D == 128) return (t & 3) | (((t >> 3) & 3) << 2);
+  if (D == 128) return ((t & 3) << 1) | (((t >> 3) & 1) << 3);
   return (t & 3) | (((t >> 3) & 1) << 2);
 }
 
@@ -73,8 +85,8 @@ PSA_HD int mf_k_lds(int t, int kk, int lg, int l16) {
   return tok * MfLayout<D>::ROW + (((kk * 4 + lg) ^ kswz<D>(tok)) << 4);
 }
 
-// The key of a K operand token depends only on the lane (token bits 0, 1, 3,
-// 4 come from l16), so the read of tile t is the tile-0 read plus a step
+// The key of a K operand token depends only on the lane (the token bits it
+// uses come from l16), so the read of tile t is the tile-0 read plus a step
 // that depends on t alone; likewise the V^T read of (kb, hf) is the (0, 0)
 // read plus a step.  The kernel holds the per-lane bases in registers and
 // adds the steps as immediates.
