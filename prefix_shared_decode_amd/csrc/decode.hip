@@ -167,52 +167,102 @@ __device__ __forceinline__ void store_ml(const DecodeParams& p, int64_t row, flo
 // Merge the E partials of (query qi, kv head kvh) in slot order and write the
 // output; one wave.  Partials hold O normalised, m (log2 units), l.  No
 // multiply-add is contracted here, so that the MFMA tile's merge in registers
-// (same operations, same order) gives the same bits.
+// (same operations, same order) gives the same bits.  Lane l covers the
+// float4 chunks l, l + 64, ... of the R x D rows.  Piece jown (if >= 0) is
+// the calling wave's own, not written to memory: its O rows are at own_o in
+// LDS (row-major, fp32), its m and l in own_m / own_l (the values its
+// partial would have held, so the result does not depend on which piece
+// merges).  With few pieces every load of every piece is issued at once.
 template <int D, int R>
-__device__ void merge_wave(const DecodeParams& p, int qi, int kvh) {
+__device__ __forceinline__ void merge_pieces(const DecodeParams& p, int qi, int kvh, int E, int jown,
+                                             const __attribute__((address_space(3))) float* own_o,
+                                             const float (&own_m)[R], const float (&own_l)[R]) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
-  const int E = p.expected[qi];
   const int64_t s0 = p.slot_off[qi];
   const auto ro = make_rsrc(p.part_o, p.part_o_bytes);
   const auto rm = make_rsrc(p.part_ml, p.part_ml_bytes);
   constexpr int C4 = D / 4;                  // float4 chunks per row
-  constexpr int NCI = (R * C4 + 63) / 64;    // chunks per lane; their loads are in flight together
+  constexpr int NCI = (R * C4 + 63) / 64;    // chunks per lane
   int hh[NCI], c4[NCI];
   bool ok[NCI];
+  float om[NCI], ol[NCI];  // the own piece's m and l for the lane's rows
 #pragma unroll
   for (int k = 0; k < NCI; ++k) {
     const int ci = lane + 64 * k;
     ok[k] = ci < R * C4;
     hh[k] = ok[k] ? ci / C4 : 0;
     c4[k] = ci % C4;
-  }
-  float M[NCI];
+    om[k] = own_m[0];
+    ol[k] = own_l[0];
 #pragma unroll
-  for (int k = 0; k < NCI; ++k) M[k] = kNoMax;
-#pragma unroll 2
-  for (int j = 0; j < E; ++j)
-#pragma unroll
-    for (int k = 0; k < NCI; ++k) {
-      const uint32_t slot = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh[k]);
-      M[k] = fmaxf(M[k], ld_coh1(rm, slot * 8u));
+    for (int h = 1; h < R; ++h) {
+      om[k] = hh[k] == h ? own_m[h] : om[k];
+      ol[k] = hh[k] == h ? own_l[h] : ol[k];
     }
-  float L[NCI];
+  }
+  auto srow = [&](int j, int k) { return (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh[k]); };
+  auto own4 = [&](int k) { return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(own_o + hh[k] * D + c4[k] * 4); };
+  float M[NCI], L[NCI];
   f32x4 acc[NCI];
 #pragma unroll
   for (int k = 0; k < NCI; ++k) {
+    M[k] = kNoMax;
     L[k] = 0.f;
     acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-#pragma unroll 2
-  for (int j = 0; j < E; ++j)
+  if (NCI <= 2 && E <= kMergeUnroll) {
+    float mj[kMergeUnroll][NCI], lj[kMergeUnroll][NCI];
+    f32x4 oj[kMergeUnroll][NCI];
+#pragma unroll
+    for (int j = 0; j < kMergeUnroll; ++j)
+#pragma unroll
+      for (int k = 0; k < NCI; ++k) {
+        mj[j][k] = om[k];
+        lj[j][k] = ol[k];
+        oj[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (j >= E) continue;
+        if (j == jown) {
+          oj[j][k] = own4(k);
+        } else {
+          mj[j][k] = ld_coh1(rm, srow(j, k) * 8u);
+          lj[j][k] = ld_coh1(rm, srow(j, k) * 8u + 4u);
+          oj[j][k] = ld_coh4(ro, (srow(j, k) * D + c4[k] * 4) * 4u);
+        }
+      }
 #pragma unroll
     for (int k = 0; k < NCI; ++k) {
-      const uint32_t slot = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh[k]);
-      const float w = ld_coh1(rm, slot * 8u + 4u) * fast_exp2(ld_coh1(rm, slot * 8u) - M[k]);
-      L[k] += w;
-      acc[k] += w * ld_coh4(ro, (slot * D + c4[k] * 4) * 4u);
+#pragma unroll
+      for (int j = 0; j < kMergeUnroll; ++j)
+        if (j < E) M[k] = fmaxf(M[k], mj[j][k]);
+#pragma unroll
+      for (int j = 0; j < kMergeUnroll; ++j) {
+        if (j >= E) continue;
+        const float w = lj[j][k] * fast_exp2(mj[j][k] - M[k]);
+        L[k] += w;
+        acc[k] += w * oj[j][k];
+      }
     }
+  } else {
+#pragma unroll 2
+    for (int j = 0; j < E; ++j)
+#pragma unroll
+      for (int k = 0; k < NCI; ++k) M[k] = fmaxf(M[k], j == jown ? om[k] : ld_coh1(rm, srow(j, k) * 8u));
+#pragma unroll 2
+    for (int j = 0; j < E; ++j)
+#pragma unroll
+      for (int k = 0; k < NCI; ++k) {
+        if (j == jown) {
+          const float w = ol[k] * fast_exp2(om[k] - M[k]);
+          L[k] += w;
+          acc[k] += w * own4(k);
+        } else {
+          const float w = ld_coh1(rm, srow(j, k) * 8u + 4u) * fast_exp2(ld_coh1(rm, srow(j, k) * 8u) - M[k]);
+          L[k] += w;
+          acc[k] += w * ld_coh4(ro, (srow(j, k) * D + c4[k] * 4) * 4u);
+        }
+      }
+  }
 #pragma unroll
   for (int k = 0; k < NCI; ++k) {
     if (!ok[k]) continue;
@@ -220,6 +270,14 @@ __device__ void merge_wave(const DecodeParams& p, int qi, int kvh) {
     store_out4(p, row * D + c4[k] * 4, acc[k] * (1.f / L[k]));
     if (c4[k] == 0) store_ml(p, row, M[k], L[k]);
   }
+}
+
+// The same merge with every piece in memory (the last arriving piece wrote
+// its partial first).
+template <int D, int R>
+__device__ void merge_wave(const DecodeParams& p, int qi, int kvh) {
+  const float none[R] = {};
+  merge_pieces<D, R>(p, qi, kvh, p.expected[qi], -1, nullptr, none, none);
 }
 
 // ----------------------------------------------------------- mat-vec tile ---
@@ -249,6 +307,13 @@ struct MvShape {
   static constexpr int TSTEP = 64 / LPT;        // token distance between slots
   static constexpr uint32_t TILE = 16 * D * EB;
   static constexpr int QBYTES = R * D * EB;     // one wave's q rows in LDS
+  // a wave's own fp32 O rows for a merge in registers: in its q rows' place
+  // when they fit (fp32), else after all waves' q rows (a wave still reading
+  // its q rows must not see them overwritten)
+  static constexpr int OBYTES = R * D * 4;
+  static constexpr int OWN_BASE = QBYTES >= OBYTES ? 0 : 4 * QBYTES;
+  static constexpr int OWN_STRIDE = QBYTES >= OBYTES ? QBYTES : OBYTES;
+  static constexpr int LDS_BYTES = OWN_BASE + 4 * OWN_STRIDE;  // for four waves
 };
 
 template <int D, int R, bool BF16>
@@ -472,8 +537,8 @@ __device__ __forceinline__ void matvec_wave(const DecodeParams& p, const WorkIte
   }
   const bool last_by_count = E > 1 && __builtin_amdgcn_readfirstlane(cval) == E - 1;
   if (E == 1 || last_by_count) {
-    if (ts == 0) {
-      if (E == 1) {
+    if (E == 1) {
+      if (ts == 0) {
 #pragma unroll
         for (int h = 0; h < R; ++h) {
           const int64_t row = (int64_t)qi * p.hq + kvh * R + h;
@@ -487,111 +552,29 @@ __device__ __forceinline__ void matvec_wave(const DecodeParams& p, const WorkIte
             }
           if (c == 0) store_ml(p, row, mtrue[h], lt[h]);
         }
-      } else {
-        // every other piece had arrived: the merge of the E partials in slot
-        // order with the operations of merge_wave (uncontracted), this
-        // wave's own partial (slot jown) taken from registers
-#pragma clang fp contract(off)
-        const auto ro = make_rsrc(p.part_o, p.part_o_bytes);
-        const auto rm = make_rsrc(p.part_ml, p.part_ml_bytes);
-        const int64_t s0 = p.slot_off[qi];
-        const int jown = slot / p.hkv - (int)s0;
-        constexpr int NQ = NCH * EPC / 4;  // float4 chunks of a head this lane holds
-        auto own4 = [&](int h, int k, int q4) {
-          const int e = k * EPC + q4 * 4;
-          return f32x4{o[h][e] * inv[h], o[h][e + 1] * inv[h], o[h][e + 2] * inv[h], o[h][e + 3] * inv[h]};
-        };
-        if (R <= 4 && E <= kMergeUnroll) {
-          // up to kMergeUnroll pieces: every load of a pass in flight together
-          float mj[R][kMergeUnroll], lj[R][kMergeUnroll];
-#pragma unroll
-          for (int h = 0; h < R; ++h)
-#pragma unroll
-            for (int j = 0; j < kMergeUnroll; ++j) {
-              mj[h][j] = mtrue[h];
-              lj[h][j] = lt[h];
-              if (j < E && j != jown) {
-                const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
-                mj[h][j] = ld_coh1(rm, srow * 8u);
-                lj[h][j] = ld_coh1(rm, srow * 8u + 4u);
-              }
-            }
-          float M[R], Ls[R];
-          f32x4 acc[R][NQ];
-#pragma unroll
-          for (int h = 0; h < R; ++h) {
-            M[h] = kNoMax;
-#pragma unroll
-            for (int j = 0; j < kMergeUnroll; ++j)
-              if (j < E) M[h] = fmaxf(M[h], mj[h][j]);
-            Ls[h] = 0.f;
-#pragma unroll
-            for (int a4 = 0; a4 < NQ; ++a4) acc[h][a4] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < kMergeUnroll; ++j) {
-              if (j >= E) continue;
-              const float w = lj[h][j] * fast_exp2(mj[h][j] - M[h]);
-              Ls[h] += w;
-              const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
-#pragma unroll
-              for (int k = 0; k < NCH; ++k)
-#pragma unroll
-                for (int q4 = 0; q4 < EPC / 4; ++q4)
-                  acc[h][k * (EPC / 4) + q4] +=
-                      w * (j == jown ? own4(h, k, q4) : ld_coh4(ro, (srow * D + (k * LPT + c) * EPC + q4 * 4) * 4u));
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < R; ++h) {
-            const int64_t row = (int64_t)qi * p.hq + kvh * R + h;
-#pragma unroll
-            for (int k = 0; k < NCH; ++k)
-#pragma unroll
-              for (int q4 = 0; q4 < EPC / 4; ++q4)
-                store_out4(p, row * D + (k * LPT + c) * EPC + q4 * 4, acc[h][k * (EPC / 4) + q4] * (1.f / Ls[h]));
-            if (c == 0) store_ml(p, row, M[h], Ls[h]);
-          }
-        } else {
-#pragma unroll
-          for (int h = 0; h < R; ++h) {
-            const int64_t row = (int64_t)qi * p.hq + kvh * R + h;
-            float M = kNoMax;
-            for (int j = 0; j < E; ++j) {
-              const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
-              M = fmaxf(M, j == jown ? mtrue[h] : ld_coh1(rm, srow * 8u));
-            }
-            float Ls = 0.f;
-            f32x4 acc[NQ];
-#pragma unroll
-            for (int a4 = 0; a4 < NQ; ++a4) acc[a4] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int j = 0; j < E; ++j) {
-              const uint32_t srow = (uint32_t)(((s0 + j) * p.hkv + kvh) * R + h);
-              if (j == jown) {
-                const float w = lt[h] * fast_exp2(mtrue[h] - M);
-                Ls += w;
-#pragma unroll
-                for (int k = 0; k < NCH; ++k)
-#pragma unroll
-                  for (int q4 = 0; q4 < EPC / 4; ++q4) acc[k * (EPC / 4) + q4] += w * own4(h, k, q4);
-              } else {
-                const float w = ld_coh1(rm, srow * 8u + 4u) * fast_exp2(ld_coh1(rm, srow * 8u) - M);
-                Ls += w;
-#pragma unroll
-                for (int k = 0; k < NCH; ++k)
-#pragma unroll
-                  for (int q4 = 0; q4 < EPC / 4; ++q4)
-                    acc[k * (EPC / 4) + q4] += w * ld_coh4(ro, (srow * D + (k * LPT + c) * EPC + q4 * 4) * 4u);
-              }
-            }
-#pragma unroll
-            for (int k = 0; k < NCH; ++k)
-#pragma unroll
-              for (int q4 = 0; q4 < EPC / 4; ++q4)
-                store_out4(p, row * D + (k * LPT + c) * EPC + q4 * 4, acc[k * (EPC / 4) + q4] * (1.f / Ls));
-            if (c == 0) store_ml(p, row, M, Ls);
-          }
-        }
       }
+    } else {
+      // every other piece had arrived: the merge of the E partials in slot
+      // order, this wave's own (slot jown) from its registers through LDS,
+      // so that all 64 lanes load the other pieces at once
+      __attribute__((address_space(3))) float* own =
+          (__attribute__((address_space(3))) float*)(smem + S::OWN_BASE + wave * S::OWN_STRIDE);
+      if (ts == 0) {
+#pragma unroll
+        for (int h = 0; h < R; ++h)
+#pragma unroll
+          for (int k = 0; k < NCH; ++k)
+#pragma unroll
+            for (int q4 = 0; q4 < EPC / 4; ++q4) {
+              const int e = k * EPC + q4 * 4;
+              *(__attribute__((address_space(3))) f32x4*)(own + h * D + (k * LPT + c) * EPC + q4 * 4) =
+                  f32x4{o[h][e] * inv[h], o[h][e + 1] * inv[h], o[h][e + 2] * inv[h], o[h][e + 3] * inv[h]};
+            }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      merge_pieces<D, R>(p, qi, kvh, E, slot / p.hkv - (int)p.slot_off[qi], own, mtrue, lt);
     }
     if (E > 1 && lane == 0) reset_counter(ctr);  // no other piece touches it in this launch
     return;
@@ -1162,7 +1145,7 @@ __device__ __forceinline__ void prefix_mfma_tile(const DecodeParams& p, const Wo
           store_out4(p, orow * D + nb * 16 + lg * 4, acc * (1.f / Ls));
         }
         if (lg == 0) store_ml(p, orow, M, Ls);
-      } else {
+      } else if (E[sl] > 3) {
         const int64_t s0 = p.slot_off[qi[sl]];
         float M = kNoMax;
         for (int j = 0; j < E[sl]; ++j) {
@@ -1191,6 +1174,51 @@ __device__ __forceinline__ void prefix_mfma_tile(const DecodeParams& p, const Wo
         for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, acc[nb] * (1.f / Ls));
         if (lg == 0) store_ml(p, orow, M, Ls);
       }
+    }
+  }
+  // three-piece merges, after the two-piece ones (whose loads are dead by then)
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    if (!(valid[sl] && E[sl] == 3 && dec[sl] == 1)) continue;
+    const int64_t orow = (int64_t)qi[sl] * p.hq + kvh * R + hh[sl];
+    {
+#pragma clang fp contract(off)
+      // the two other pieces' m, l and O rows, all loads in flight together
+      // (one slice at a time: the scheduler is fenced around it)
+      __builtin_amdgcn_sched_barrier(0);
+      const int64_t s0 = p.slot_off[qi[sl]];
+      const int ja = jslot == 0 ? 1 : 0, jb = jslot == 2 ? 1 : 2;  // the other slots, in order
+      float mo2[2], lo2[2];
+      f32x4 oo2[2][NB];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const uint32_t srow = (uint32_t)(((s0 + (x ? jb : ja)) * p.hkv + kvh) * R + hh[sl]);
+        mo2[x] = ld_coh1(rm, srow * 8u);
+        lo2[x] = ld_coh1(rm, srow * 8u + 4u);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) oo2[x][nb] = ld_coh4(ro, (srow * D + nb * 16 + lg * 4) * 4u);
+      }
+      // slot j's piece: this tile's own, or the x-th other
+      auto xof = [&](int j) { return j == ja ? 0 : 1; };
+      float M = kNoMax;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) M = fmaxf(M, j == jslot ? mt[sl] : mo2[xof(j)]);
+      float w[3], Ls = 0.f;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        w[j] = j == jslot ? lt[sl] * fast_exp2(mt[sl] - M) : lo2[xof(j)] * fast_exp2(mo2[xof(j)] - M);
+        Ls += w[j];
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const f32x4 own = st.o[sl][nb] * inv[sl];
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 3; ++j) acc += w[j] * (j == jslot ? own : oo2[xof(j)][nb]);
+        store_out4(p, orow * D + nb * 16 + lg * 4, acc * (1.f / Ls));
+      }
+      if (lg == 0) store_ml(p, orow, M, Ls);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // the last arrivers among the partials written above merge
@@ -1246,7 +1274,8 @@ __device__ __forceinline__ void poison_outputs(const DecodeParams& p) {
 // tell a stage's reads from the copy into the other stage.
 template <int D, int R, bool BF16>
 struct Lds {
-  static constexpr int MV = kWaves * MvShape<D, R, BF16>::QBYTES;
+  static constexpr int MV = MvShape<D, R, BF16>::LDS_BYTES;
+  static_assert(kWaves == 4, "the mat-vec LDS layout assumes four waves");
   static constexpr int MF = BF16 ? MfShape<D>::STAGE : 16;
   static constexpr int STAGE0 = MV > MF ? MV : MF;
 };
