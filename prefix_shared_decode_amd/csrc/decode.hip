@@ -119,7 +119,10 @@ constexpr int kMvPages = PSA_MV_PAGES;  // mat-vec tile: bf16 pages of K and V i
 // the register budget, so that shape keeps one page in flight)
 template <int D, int R, bool BF16>
 constexpr int mv_pages() { return BF16 || D * R < 1024 ? kMvPages : 1; }
-constexpr int kMergeUnroll = 4;         // in-register merges of up to this many pieces load in one pass
+#ifndef PSA_MERGE_BATCH
+#define PSA_MERGE_BATCH 8
+#endif
+constexpr int kMergeUnroll = PSA_MERGE_BATCH;  // merges of up to this many pieces load every piece in one pass
 constexpr int kSc1 = 16;  // cache policy: coherent at device (agent) scope
 constexpr int kNt = 2;    // cache policy: non-temporal (streamed once; keeps reused prefix K/V and
                           // partials from being evicted by the distinct KV stream)
@@ -1145,7 +1148,7 @@ __device__ __forceinline__ void prefix_mfma_tile(const DecodeParams& p, const Wo
           store_out4(p, orow * D + nb * 16 + lg * 4, acc * (1.f / Ls));
         }
         if (lg == 0) store_ml(p, orow, M, Ls);
-      } else if (E[sl] > 3) {
+      } else if (E[sl] > kMergeUnroll) {
         const int64_t s0 = p.slot_off[qi[sl]];
         float M = kNoMax;
         for (int j = 0; j < E[sl]; ++j) {
@@ -1220,6 +1223,56 @@ __device__ __forceinline__ void prefix_mfma_tile(const DecodeParams& p, const Wo
       if (lg == 0) store_ml(p, orow, M, Ls);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  // merges of four or more pieces, last (one slice at a time)
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    if (!(valid[sl] && E[sl] > 3 && E[sl] <= kMergeUnroll && dec[sl] == 1)) continue;
+    const int64_t orow = (int64_t)qi[sl] * p.hq + kvh * R + hh[sl];
+    __builtin_amdgcn_sched_barrier(0);
+    {
+#pragma clang fp contract(off)
+      // m and l of every piece in one batch of loads, then the O rows piece
+      // by piece (slot order throughout)
+      const int64_t s0 = p.slot_off[qi[sl]];
+      const int En = E[sl];
+      auto srow_of = [&](int j) { return (uint32_t)(((s0 + j) * p.hkv + kvh) * R + hh[sl]); };
+      float mj[kMergeUnroll], lj[kMergeUnroll];
+#pragma unroll
+      for (int j = 0; j < kMergeUnroll; ++j) {
+        mj[j] = mt[sl];
+        lj[j] = lt[sl];
+        if (j < En && j != jslot) {
+          mj[j] = ld_coh1(rm, srow_of(j) * 8u);
+          lj[j] = ld_coh1(rm, srow_of(j) * 8u + 4u);
+        }
+      }
+      float M = kNoMax;
+#pragma unroll
+      for (int j = 0; j < kMergeUnroll; ++j)
+        if (j < En) M = fmaxf(M, mj[j]);
+      float Ls = 0.f;
+      f32x4 acc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kMergeUnroll; ++j) {
+        if (j >= En) break;
+        const float w = lj[j] * fast_exp2(mj[j] - M);
+        Ls += w;
+        if (j == jslot) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[nb] += w * (st.o[sl][nb] * inv[sl]);
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[nb] += w * ld_coh4(ro, (srow_of(j) * D + nb * 16 + lg * 4) * 4u);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) store_out4(p, orow * D + nb * 16 + lg * 4, acc[nb] * (1.f / Ls));
+      if (lg == 0) store_ml(p, orow, M, Ls);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   // the last arrivers among the partials written above merge
   if (any_partial) {
