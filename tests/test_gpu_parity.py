@@ -397,6 +397,48 @@ def test_deterministic_and_reusable_workspace():
     assert torch.equal(out3, ref)
 
 
+@pytest.mark.parametrize("case", ["two_level_three_pieces", "many_prefix_chunks"])
+def test_merge_paths_give_the_same_bits(case):
+    """Queries of three pieces (root tile, own tile, distinct part) and of
+    five to twelve (1024- and 2048-token prefixes in 256-token chunks plus
+    distinct parts in 128-token chunks):
+    whichever piece arrives last merges, in registers or from memory, in one
+    batch of loads or piece by piece, so repeated launches and plans that
+    reorder the work must give the same bits, and match the oracle."""
+    import torch
+
+    if case == "two_level_three_pieces":
+        wl = build_two_level("merge3", 32, 8, 128, "bf16", 2, 256, 3, 512, 6, (16, 200), seed=9)
+        batch, _ = P.psa_flatten_prefix_tree(wl.tree)
+        kw = {}
+        ctx = oracle.flatten_tree(wl.tree, [-1] * len(wl.tree["query_node"]))
+    else:
+        wl = build_single_level("merge10", 32, 8, 128, "bf16", [(1024, 6, (100, 400)), (2048, 6, (100, 400))],
+                                (2, (50, 300)), seed=10)
+        batch = wl.batch
+        kw = dict(prefix_chunk_tokens=256, distinct_chunk_tokens=128)
+        ctx = None
+    q, k, v = values(wl)
+    log(f"case {case}: repeats and reordered plans, bit for bit")
+    step, out, m, l = run(wl, batch, q, k, v, **kw)
+    ref, mref, lref = out.clone(), m.clone(), l.clone()
+    if ctx is not None:
+        O, M, L = oracle.decode_attention(to_host64(q), to_host64(k), to_host64(v), ctx)
+    else:
+        O, M, L = oracle_all(wl, batch, q, k, v)
+    assert_close(to_host64(out), O, "bf16", case)
+    assert_lse_close(m, l, M, L, 2e-4)
+    for _ in range(10):
+        for t in (out, m, l):
+            t.fill_(float("nan"))
+        step(q, k, v, out, m, l)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(m, mref) and torch.equal(l, lref)
+    for flags in (P.NO_XCD_ORDER, P.NO_TILE_PAIRS, P.DEBUG_POISON):
+        _, o2, m2, l2 = run(wl, batch, q, k, v, flags=flags, **kw)
+        assert torch.equal(o2, ref) and torch.equal(m2, mref) and torch.equal(l2, lref), flags
+
+
 # ---------------- full-size workloads, whole output ----------------
 
 FULL = ["llama3_8b_8x100", "longchat13b_1x256", "no_sharing_512", "two_level_4x16x16", "mixed_7prefill_256decode"]
