@@ -481,17 +481,26 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
     // unit shares those CUs' load path with the tiles' copies, and the tiles'
     // two waves per SIMD hide each other's latencies.
     constexpr int kCusPerXcd = 32;
+    std::vector<int32_t> set_size(next_set + 1, 0);  // units per set (an MFMA set: row tiles of one chunk)
+    for (const Unit& u : units) ++set_size[u.set];
     if (!(o.flags & PSA_PLAN_NO_TILE_PAIRS)) {
       for (auto& qq : q) {
         size_t np = 0;
         while (np < qq.size() && units[qq[np]].it[0].kind % 256 == ITEM_PREFIX_MFMA) ++np;
         if (np > 2 * (size_t)kCusPerXcd && qq.size() > np) {
-          // More tiles than one round of pairs: spread them evenly over the
-          // first 3/4 of the queue, so that MFMA tiles (latency bound) and
-          // mat-vec units (HBM bound) run side by side instead of one phase
-          // after the other, and short mat-vec units end the launch.
-          // (Flattened 4x16x16 with family tiles: 0.254 ms; tiles first
-          // 0.270, spread over the whole queue 0.270.)
+          // More tiles than one round of pairs.  Tiles whose prefix chunk
+          // has several row tiles read it from L2 and are bound by their
+          // compute: spread evenly over the first 3/4 of the queue, they run
+          // beside the HBM-bound mat-vec units instead of in a phase of
+          // their own, and short mat-vec units end the launch (7 prefill
+          // chunks + 256 decode queries: 0.149 ms, tiles first 0.162).
+          // Tiles that are their chunk's only row tile stream it from HBM
+          // themselves: when they are the majority, plain longest first
+          // (flattened 4x16x16, two thirds of its tiles: 0.239 ms, spread
+          // 0.244).
+          size_t streaming = 0;
+          for (size_t k = 0; k < np; ++k) streaming += set_size[units[qq[k]].set] == 1;
+          if (2 * streaming > np) continue;
           const size_t n = qq.size();
           const size_t span = std::max(np, (size_t)(0.75 * (double)n));
           std::vector<int64_t> re;
