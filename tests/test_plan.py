@@ -472,14 +472,31 @@ def test_mfma_tiles_start_two_to_a_cu():
         _check_coverage(wl, plan)
 
 
-def test_mfma_tiles_spread_when_more_than_a_round_of_pairs():
-    """The flattened two-level shape without family tiles has 128 MFMA tiles
-    per XCD queue (more than two per CU): they are spread evenly over the
-    first three quarters of each queue, interleaved with the mat-vec units,
-    instead of leading it;
-    NO_TILE_PAIRS keeps them first.  Both orders cover every (query, kv head)
-    exactly."""
+def test_mfma_tiles_beyond_a_round_of_pairs():
+    """More than two MFMA tiles per CU in an XCD queue.  Tiles that share
+    their prefix chunk with other row tiles (the prefill chunks of the mixed
+    preset: compute bound, read from L2) are spread evenly over the first
+    three quarters of each queue, interleaved with the mat-vec units; tiles
+    that are their chunk's only row tile (the flattened two-level shape
+    without shared pages: each streams its own pages) lead the queue, longest
+    first.  NO_TILE_PAIRS keeps every tile first.  Every order covers every
+    (query, kv head) exactly."""
     from workloads import make_workload
+
+    wl = make_workload("mixed_7prefill_256decode")
+    plan = P.psa_build_plan(_cfg(wl), wl.batch)
+    kinds = plan.items()[::4, 0] & 0xFF
+    for x in range(8):
+        local = kinds[x::8]
+        pos = np.nonzero(local == 2)[0]
+        n, npx = len(local), len(pos)
+        span = int(0.75 * n)
+        assert npx > 64 and pos[0] == 0 and pos[-1] < span
+        # tile k sits where k / npx of the span is reached: never two in a row
+        # for long, never far from its even place
+        want = np.ceil(np.arange(npx) * span / npx)
+        assert np.abs(pos - want).max() <= 1, x
+    _check_coverage(wl, plan)
 
     wl = make_workload("two_level_4x16x16")
     batch, _ = P.psa_flatten_prefix_tree(wl.tree)
@@ -491,20 +508,12 @@ def test_mfma_tiles_spread_when_more_than_a_round_of_pairs():
     fw.__dict__.update(wl.__dict__)
     fw.batch = batch
     fw.num_queries = len(batch["query_group"])
-    plan = P.psa_build_plan(_cfg(wl), batch, flags=P.NO_PAGE_SHARING)
-    kinds = plan.items()[::4, 0] & 0xFF
-    for x in range(8):
-        local = kinds[x::8]
-        pos = np.nonzero(local == 2)[0]
-        n, npx = len(local), len(pos)
-        assert npx == 128 and pos[0] == 0
-        gaps = np.diff(pos)
-        span = int(0.75 * n)  # spread over the first three quarters of the queue
-        assert gaps.max() <= -(-span // npx) and gaps.min() >= span // npx - 1 and pos[-1] < span
-    _check_coverage(fw, plan)
-    kinds = P.psa_build_plan(_cfg(wl), batch, flags=P.NO_TILE_PAIRS | P.NO_PAGE_SHARING).items()[::4, 0] & 0xFF
-    for x in range(8):
-        assert list(np.nonzero(kinds[x::8] == 2)[0]) == list(range(128))
+    for flags in (P.NO_PAGE_SHARING, P.NO_TILE_PAIRS | P.NO_PAGE_SHARING):
+        plan = P.psa_build_plan(_cfg(wl), batch, flags=flags)
+        kinds = plan.items()[::4, 0] & 0xFF
+        for x in range(8):
+            assert list(np.nonzero(kinds[x::8] == 2)[0]) == list(range(128)), (flags, x)
+        _check_coverage(fw, plan)
 
 
 def _flat(wl):
