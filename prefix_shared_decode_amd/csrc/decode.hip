@@ -297,7 +297,8 @@ __device__ void merge_wave(const DecodeParams& p, int qi, int kvh) {
 // included, never meets a weight).  Pages are loaded non-temporal: each byte is read once.
 // P is rounded to bf16 for the P.V dot products; O is normalised by the sum of those rounded
 // weights (a convex combination of V rows), while the reported l is the exact fp32 sum.
-// q is staged once through LDS (per wave) and re-read per page.
+// q is staged once through LDS (per wave); bf16 rows of up to 512 elements
+// stay in registers for the page loop, larger ones are re-read per page.
 template <int D, int R, bool BF16>
 struct MvShape {
   static constexpr int EB = BF16 ? 2 : 4;
@@ -377,9 +378,11 @@ __device__ __forceinline__ void matvec_wave(const DecodeParams& p, const WorkIte
   // units, masked tokens -inf); on the first page of the first pass, the
   // head's reference max; the exponentials against it; P.V.
   auto page = [&](const PageRegs<D, R, BF16>& b, int j, bool set_ref, bool& over) {
-    // re-read q from LDS every page (an opaque offset keeps the reads in the loop)
+    // q from LDS: held in registers across the page loop where R * D <= 512
+    // bf16 elements (32 VGPRs); re-read every page otherwise (an opaque
+    // offset keeps the reads in the loop), where holding it would spill
     uint32_t qoff = (uint32_t)(c * EPC * S::EB);
-    asm volatile("" : "+v"(qoff));
+    if constexpr (!(BF16 && R * D <= 512)) asm volatile("" : "+v"(qoff));
     const int tok0 = tb + j * 16 + ts;
 #pragma unroll
     for (int h = 0; h < R; ++h) {
