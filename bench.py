@@ -153,50 +153,72 @@ def host_identification(P, reps=3):
             "context": "the pages quote 1.51 s for 8000 requests (Python, host CPU), tree build to group list"}
 
 
-def trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, path):
-    """One traced launch (after a cache flush): per-kind unit durations and a
-    timeline of how many units of each kind run at once (10 us bins)."""
+def trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, path, wl, launches=3):
+    """Traced launches (a cache flush before each): per unit its start, end
+    and XCD (s_memrealtime, 100 MHz).  Reported per launch: per-kind unit
+    durations, how many units of each kind run at once (10 us bins), each
+    XCD's last end and summed unit time, and the mat-vec units' KV rate over
+    time, estimated by spreading each unit's bytes evenly over its life (an
+    estimate: good for comparing phases and runs, not an absolute rate)."""
     import numpy as np
     import torch
 
     units = int(info["num_items"])
-    tr = torch.zeros(units * 4, dtype=torch.int64, device="cuda")
-    if flush is not None:
-        torch.sum(flush, dim=None, out=sink)
-    P.psa_decode_attention(plan, q, k, v, out, ws, trace=tr)
-    torch.cuda.synchronize()
-    t = tr.view(units, 4).cpu().numpy()
-    np.save(path + ".npy", t)  # raw records: start, end, HW_ID | XCC_ID << 32, kind
-    ok = (t[:, 0] > 0) & (t[:, 1] >= t[:, 0])
-    if not ok.all():
-        log(f"trace: {int((~ok).sum())} of {units} units without a valid record, e.g. {t[~ok][:3].tolist()}")
-        t = t[ok]
-    if len(t) == 0:
-        return
-    t0 = t[:, 0].min()
-    start = (t[:, 0] - t0) / 100.0  # 100 MHz clock -> us
-    end = (t[:, 1] - t0) / 100.0
-    kind = t[:, 3]
+    it = np.asarray(plan.items()).reshape(units, 4, 8)
+    kind_of = it[:, 0, 0] & 0xFF
+    tok_bytes = wl.head_dim * (2 if wl.dtype == "bf16" else 4) * 2  # K and V of one token, one kv head
+    mv_tokens = np.zeros(units)
+    for w in range(4):
+        mv_tokens += np.where((it[:, w, 0] & 0xFF) == 1, it[:, w, 4] - it[:, w, 3], 0)
     names = {0: "nop", 1: "matvec", 2: "mfma_prefix", 3: "empty"}
-    res = {"units": units, "span_us": float(end.max()), "kinds": {}}
-    bins = np.arange(0.0, float(end.max()) + 10.0, 10.0)
-    for kd in np.unique(kind):
-        sel = kind == kd
-        dur = end[sel] - start[sel]
-        active = [int(((start[sel] < b + 10.0) & (end[sel] > b)).sum()) for b in bins]
-        res["kinds"][names.get(int(kd), str(kd))] = {
-            "count": int(sel.sum()), "dur_us_mean": float(dur.mean()), "dur_us_p50": float(np.median(dur)),
-            "dur_us_max": float(dur.max()), "first_start_us": float(start[sel].min()),
-            "last_start_us": float(start[sel].max()), "last_end_us": float(end[sel].max()),
-            "active_per_10us": active}
-    xcc = (t[:, 2] >> 32) & 0xF
-    res["units_per_xcc"] = [int((xcc == x).sum()) for x in range(8)]
+    res = {"units": units, "launches": []}
+    for li in range(launches):
+        tr = torch.zeros(units * 4, dtype=torch.int64, device="cuda")
+        if flush is not None:
+            torch.sum(flush, dim=None, out=sink)
+        P.psa_decode_attention(plan, q, k, v, out, ws, trace=tr)
+        torch.cuda.synchronize()
+        t = tr.view(units, 4).cpu().numpy()
+        if li == 0:
+            np.save(path + ".npy", t)  # raw records of the first launch: start, end, HW_ID | XCC_ID << 32, kind
+        ok = (t[:, 0] > 0) & (t[:, 1] >= t[:, 0])
+        if not ok.all():
+            log(f"trace: {int((~ok).sum())} of {units} units without a valid record, e.g. {t[~ok][:3].tolist()}")
+            continue
+        t0 = t[:, 0].min()
+        start = (t[:, 0] - t0) / 100.0  # 100 MHz clock -> us
+        end = (t[:, 1] - t0) / 100.0
+        kind = t[:, 3]
+        span = float(end.max())
+        bins = np.arange(0.0, span + 10.0, 10.0)
+        rec = {"span_us": span, "kinds": {}}
+        for kd in np.unique(kind):
+            sel = kind == kd
+            dur = end[sel] - start[sel]
+            rec["kinds"][names.get(int(kd), str(kd))] = {
+                "count": int(sel.sum()), "dur_us_mean": float(dur.mean()), "dur_us_p50": float(np.median(dur)),
+                "dur_us_max": float(dur.max()), "first_start_us": float(start[sel].min()),
+                "last_start_us": float(start[sel].max()), "last_end_us": float(end[sel].max()),
+                "active_per_10us": [int(((start[sel] < b + 10.0) & (end[sel] > b)).sum()) for b in bins]}
+        xcc = (t[:, 2] >> 32) & 0xF
+        rec["xcd"] = [{"units": int((xcc == x).sum()), "last_end_us": float(end[xcc == x].max()),
+                       "unit_us": float((end - start)[xcc == x].sum())} for x in range(8) if (xcc == x).any()]
+        rate = np.zeros(len(bins))
+        for u in np.where((kind_of == 1) & (end > start))[0]:
+            r = mv_tokens[u] * tok_bytes / (end[u] - start[u])  # bytes per us
+            lo, hi = start[u], end[u]
+            for j in range(int(lo // 10), min(int(hi // 10) + 1, len(bins))):
+                rate[j] += r * max(0.0, min(hi, bins[j] + 10.0) - max(lo, bins[j])) / 10.0
+        rec["matvec_TBps_per_10us_estimate"] = [round(float(x) / 1e6, 3) for x in rate]
+        res["launches"].append(rec)
+        log(f"trace launch {li}: span {span:.1f} us; XCD last ends "
+            + " ".join(f"{x['last_end_us']:.0f}" for x in rec["xcd"]))
+        for name, r in rec["kinds"].items():
+            log(f"  {name}: n={r['count']} dur mean {r['dur_us_mean']:.1f} us max {r['dur_us_max']:.1f}, "
+                f"starts {r['first_start_us']:.1f}..{r['last_start_us']:.1f}, last end {r['last_end_us']:.1f} us")
+        log("  mat-vec TB/s per 10 us (estimate): " + " ".join(f"{x:.1f}" for x in rec["matvec_TBps_per_10us_estimate"]))
     with open(path, "w") as f:
         json.dump(res, f)
-    for name, r in res["kinds"].items():
-        log(f"trace {name}: n={r['count']} dur mean {r['dur_us_mean']:.1f} us max {r['dur_us_max']:.1f}, "
-            f"starts {r['first_start_us']:.1f}..{r['last_start_us']:.1f}, last end {r['last_end_us']:.1f} us")
-    log(f"trace span {res['span_us']:.1f} us")
 
 
 def timed(fn, steps, flush, sink):
@@ -487,7 +509,7 @@ def run_one(args):
         log("cpu baseline: timing the fp64 oracle on a sample")
         rec["cpu_baseline"] = cpu_baseline(wl, batch, q, k, v, args.cpu_seconds, 30.0)
     if args.trace:
-        trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, args.trace)
+        trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, args.trace, wl)
     rec["context"] = {
         "note": "figures quoted by the pages; end-to-end serving speedups on other hardware, not measurements "
                 "of this kernel, so no vs_baseline is derived from them",

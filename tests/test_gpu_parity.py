@@ -397,6 +397,37 @@ def test_deterministic_and_reusable_workspace():
     assert torch.equal(out3, ref)
 
 
+def test_traced_launch_records_every_unit():
+    """The traced entry point (per-unit timing for the bench's timelines)
+    gives the untraced launch's bits and one valid record per unit: start
+    <= end, an XCD id below 8, and the unit's kind from the plan."""
+    import torch
+
+    wl = build_single_level("trace", 32, 8, 128, "bf16", [(400, 30, (0, 300))], (4, (1, 900)), seed=7)
+    q, k, v = values(wl)
+    log("case traced launch: records and bits")
+    plan = P.psa_build_plan(P.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.dtype),
+                            wl.batch, prefix_chunk_tokens=128, distinct_chunk_tokens=128)
+    info = plan.info()
+    ws = torch.empty(max(int(info["workspace_bytes"]), 256), dtype=torch.uint8, device="cuda")
+    P.psa_plan_upload(plan, ws)
+    n = len(wl.batch["query_group"])
+    outs = []
+    units = int(info["num_items"])
+    tr = torch.zeros(units * 4, dtype=torch.int64, device="cuda")
+    for traced in (False, True):
+        o = torch.full((n, wl.num_q_heads, wl.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        P.psa_decode_attention(plan, q, k, v, o, ws, trace=tr if traced else None)
+        torch.cuda.synchronize()
+        outs.append(o)
+    assert torch.equal(outs[0], outs[1])
+    t = tr.view(units, 4).cpu().numpy()
+    kinds = np.asarray(plan.items()).reshape(units, 4, 8)[:, 0, 0] & 0xFF
+    assert (t[:, 0] > 0).all() and (t[:, 1] >= t[:, 0]).all()
+    assert (((t[:, 2] >> 32) & 0xF) < 8).all()
+    assert np.array_equal(t[:, 3], kinds)
+
+
 @pytest.mark.parametrize("case", ["two_level_three_pieces", "many_prefix_chunks"])
 def test_merge_paths_give_the_same_bits(case):
     """Queries of three pieces (root tile, own tile, distinct part) and of
