@@ -278,6 +278,19 @@ def test_fp32_larger_and_scale():
     assert_close(to_host64(out), O, "f32", "f32 scale 0.3")
 
 
+@pytest.mark.parametrize("r,d", [(1, 64), (4, 64), (8, 64), (1, 128), (4, 128), (8, 128)])
+def test_fp32_every_head_shape(r, d):
+    """fp32 K/V (mat-vec tiles only: the MFMA tile is bf16) at every GQA ratio
+    and head dim the library instantiates besides r 2, which the other fp32
+    cases cover; d 128 with r 8 keeps one page in flight."""
+    wl = build_single_level(f"f32_r{r}_d{d}", 2 * r, 2, d, "f32", [(150, 5, (0, 70)), (33, 2, (1, 20))],
+                            (2, (1, 300)), seed=30 + r + d)
+    q, k, v = values(wl)
+    _check_full(wl, wl.batch, q, k, v, f"f32 r{r} d{d}")
+    _check_full(wl, wl.batch, q, k, v, f"f32 r{r} d{d} small chunks", prefix_chunk_tokens=64,
+                distinct_chunk_tokens=32)
+
+
 def test_bf16_output():
     wl = build_single_level("bf16_out", 32, 8, 128, "bf16", [(256, 12, (4, 64))], (2, (1, 99)), seed=9)
     q, k, v = values(wl)
