@@ -291,6 +291,18 @@ def test_fp32_every_head_shape(r, d):
                 distinct_chunk_tokens=32)
 
 
+def test_bf16_r2_d64():
+    """bf16 at GQA ratio 2 and head dim 64 (the one bf16 instantiation no other
+    case reaches): MFMA tiles, small chunks, mat-vec only."""
+    wl = build_single_level("bf16_r2_d64", 8, 4, 64, "bf16", [(300, 20, (0, 80)), (70, 3, (1, 30))],
+                            (2, (1, 200)), seed=44)
+    q, k, v = values(wl)
+    _check_full(wl, wl.batch, q, k, v, "bf16 r2 d64")
+    _check_full(wl, wl.batch, q, k, v, "bf16 r2 d64 small chunks", prefix_chunk_tokens=64, distinct_chunk_tokens=32,
+                mfma_tile_rows=32)
+    _check_full(wl, wl.batch, q, k, v, "bf16 r2 d64 mat-vec only", flags=P.FORCE_MATVEC)
+
+
 def test_bf16_output():
     wl = build_single_level("bf16_out", 32, 8, 128, "bf16", [(256, 12, (4, 64))], (2, (1, 99)), seed=9)
     q, k, v = values(wl)
