@@ -718,29 +718,34 @@ __device__ __forceinline__ void mf_block(MfRows<D>& st, const lds_char* Ks, cons
   for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
     for (int t = 0; t < 4; ++t) s[sl][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // K operands of token tiles t and t + 1 are in flight while tile t - 1's
-  // MFMAs issue; one piece of the next block's copy follows each tile's
-  // MFMAs, so that a stall on issuing it (the load path is shared with the
-  // other workgroup on the CU) leaves queued matrix work behind it.
-  bf16x8 a[2][KK];
-  auto kread = [&](int t) {
+  // The QK product by k-step: the MFMAs of one k-step over the four token
+  // tiles and NS slices are 4 NS independent accumulation chains (a single
+  // wave issues back-to-back MFMAs at full rate only with about eight in
+  // flight; a chain's next MFMA waits for the previous result).  The K
+  // operands of k-steps kk and kk + 1 are in flight while kk - 1's MFMAs
+  // issue; pieces of the next block's copy follow each k-step's MFMAs, so
+  // that a stall on issuing one (the load path is shared with the other
+  // workgroup on the CU) leaves queued matrix work behind it.
+  bf16x8 a[2][4];
+  auto kread = [&](int kk) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      a[t & 1][kk] = *(const __attribute__((address_space(3))) bf16x8*)(Ks + st.koff[kk] + mf_k_step<D>(t));
+    for (int t = 0; t < 4; ++t)
+      a[kk & 1][t] = *(const __attribute__((address_space(3))) bf16x8*)(Ks + st.koff[kk] + mf_k_step<D>(t));
   };
   kread(0);
-  kread(1);
+  if (KK > 1) kread(1);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int kk = 0; kk < KK; ++kk) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl)
-        s[sl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t & 1][kk], st.qb[sl][kk], s[sl][t], 0, 0, 0);
+        s[sl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk & 1][t], st.qb[sl][kk], s[sl][t], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    if (t + 2 < 4) kread(t + 2);
-    copy(t);
+    if (kk + 2 < KK) kread(kk + 2);
+#pragma unroll
+    for (int c = kk * 4 / KK; c < (kk + 1) * 4 / KK; ++c) copy(c);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (valid < 64 || limits) {  // last block of the chunk, or rows with their own limits
