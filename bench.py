@@ -274,8 +274,26 @@ def measured_peaks(P, buf, reps):
         best[name] = min(ts)
     return {"hbm_read_GBps": nbytes / (best["read"] / 1e3) / 1e9, "read_bytes": nbytes,
             "mfma_bf16_TFLOPs": flops / (best["mfma"] / 1e3) / 1e12,
+            "issue_cycles": issue_rates(P),
             "note": "best of %d launches each: a non-temporal 16-byte-load read of %d MiB (one contiguous span per workgroup), and 2048x4 waves of "
                     "%d dependent v_mfma_f32_16x16x32_bf16" % (reps, nbytes >> 20, iters)}
+
+
+def issue_rates(P, iters=1024):
+    """Core-clock cycles one wave (alone on its SIMD) spends per instruction of
+    each issue-probe pattern (psa_debug_issue_probe; median over all waves of
+    the second of two launches; pattern 7 per MFMA with its share of softmax
+    work)."""
+    import torch
+
+    cyc = torch.empty(1024, dtype=torch.int64, device="cuda")
+    row = {}
+    for pat, (name, per_iter) in P.ISSUE_PATTERNS.items():
+        P.psa_debug_issue_probe(pat, cyc, iters)
+        P.psa_debug_issue_probe(pat, cyc, iters)
+        torch.cuda.synchronize()
+        row[name] = round(float(cyc.double().median()) / (iters * per_iter), 2)
+    return row
 
 
 def components(P, cfg, batch, wl, q, k, v, flush, sink, steps, fused_ms, peaks=None):

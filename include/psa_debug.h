@@ -66,6 +66,19 @@ psa_status psa_debug_read_peak(const void* d_buf, size_t bytes, uint32_t* d_sink
                                void* stream);
 psa_status psa_debug_mfma_peak(float* d_out, int64_t out_capacity, int32_t iters, void* stream);
 
+/* Instruction issue rates of one wave (diagnostics): 256 workgroups of 4
+ * waves, one workgroup per CU, so that each SIMD holds one wave; each wave
+ * times `iters` iterations of one pattern with s_memtime (core clock) and
+ * writes the cycles to d_cycles[wave] (int64, capacity >= 1024 entries).
+ * Per iteration, pattern
+ *   0..4: 16 v_mfma_f32_16x16x32_bf16 in 16, 8, 4, 2 or 1 independent chains;
+ *   5:    16 independent v_fma_f32;   6: 8 independent v_exp_f32;
+ *   7:    16 MFMAs in 8 chains with 32 v_fma_f32 and 8 v_exp_f32 between
+ *         them (the softmax work the MFMA prefix tile issues per MFMA).
+ * Errors: NULL or non-device pointer, pattern out of range, iters <= 0,
+ * capacity too small. */
+psa_status psa_debug_issue_probe(int32_t pattern, int64_t* d_cycles, int64_t capacity, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

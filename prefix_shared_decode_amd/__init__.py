@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     DEBUG_POISON,
     DISTINCT_ONLY,
     EXPORTS,
+    ISSUE_PATTERNS,
     FORCE_MATVEC,
     LIB_PATH,
     NO_TILE_PAIRS,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     lib,
     make_config,
     psa_build_plan,
+    psa_debug_issue_probe,
     psa_debug_mfma_peak,
     psa_debug_read_peak,
     psa_decode_attention,

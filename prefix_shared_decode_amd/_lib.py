@@ -26,7 +26,7 @@ STATUS = {0: "PSA_OK", 1: "PSA_ERR_INVALID_ARGUMENT", 2: "PSA_ERR_UNSUPPORTED", 
 EXPORTS = ["psa_build_plan", "psa_plan_get_info", "psa_plan_upload", "psa_decode_attention", "psa_merge",
            "psa_flatten_prefix_tree", "psa_batch_owned_view", "psa_free_batch", "psa_destroy_plan",
            "psa_last_error", "psa_version", "psa_plan_debug_items", "psa_plan_debug_queries",
-           "psa_decode_attention_traced", "psa_debug_read_peak", "psa_debug_mfma_peak",
+           "psa_decode_attention_traced", "psa_debug_read_peak", "psa_debug_mfma_peak", "psa_debug_issue_probe",
            "psa_identify_prefix_groups", "psa_prefix_groups_view", "psa_free_prefix_groups",
            "psa_decode_attention_noalloc", "psa_plan_debug_members"]
 
@@ -121,6 +121,7 @@ def lib():
         L.psa_decode_attention_traced.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp, C.c_int64, vp]
         L.psa_debug_read_peak.argtypes = [vp, C.c_size_t, vp, C.c_int64, vp]
         L.psa_debug_mfma_peak.argtypes = [vp, C.c_int64, C.c_int32, vp]
+        L.psa_debug_issue_probe.argtypes = [C.c_int32, vp, C.c_int64, C.c_int32, vp]
         for name in EXPORTS:
             fn = getattr(L, name)
             if fn.restype is C.c_int and name not in ("psa_version",):
@@ -325,6 +326,19 @@ def psa_debug_mfma_peak(out, iters, stream=None):
     float32 device tensor of >= 2048 * 256 entries.  Returns the flops it does."""
     _check(lib().psa_debug_mfma_peak(_dev_ptr(out, "out"), out.numel(), int(iters), _stream_ptr(stream)))
     return 2048.0 * 4 * iters * 16384
+
+
+# instructions per iteration of each issue-probe pattern (include/psa_debug.h)
+ISSUE_PATTERNS = {0: ("mfma, 16 chains", 16), 1: ("mfma, 8 chains", 16), 2: ("mfma, 4 chains", 16),
+                  3: ("mfma, 2 chains", 16), 4: ("mfma, 1 chain", 16), 5: ("v_fma_f32", 16), 6: ("v_exp_f32", 8),
+                  7: ("mfma (8 chains) + 2 fma + 1/2 exp", 16)}
+
+
+def psa_debug_issue_probe(pattern, cycles, iters, stream=None):
+    """One launch of an issue-rate pattern (include/psa_debug.h); ``cycles`` is an
+    int64 device tensor of >= 1024 entries."""
+    _check(lib().psa_debug_issue_probe(int(pattern), _dev_ptr(cycles, "cycles"), cycles.numel(), int(iters),
+                                       _stream_ptr(stream)))
 
 
 def psa_merge(o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, stream=None):

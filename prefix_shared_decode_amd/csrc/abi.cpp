@@ -17,6 +17,7 @@ namespace psa {
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int r, bool bf16, hipStream_t s);
 hipError_t launch_read_peak(const void* buf, uint32_t bytes, uint32_t* sink, int blocks, hipStream_t s);
 hipError_t launch_mfma_peak(float* out, int iters, int blocks, hipStream_t s);
+hipError_t launch_issue_probe(int pattern, int64_t* cycles, int iters, int blocks, hipStream_t s);
 hipError_t launch_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* m_a, const float* l_a,
                         const float* o_b, const float* m_b, const float* l_b, float* o, float* m, float* l,
                         hipStream_t s);
@@ -403,6 +404,24 @@ psa_status psa_debug_mfma_peak(float* d_out, int64_t out_capacity, int32_t iters
   if (st != PSA_OK) return st;
   e = psa::launch_mfma_peak(d_out, iters, kPeakBlocks, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return psa::hip_fail(e, "mfma peak kernel launch");
+  return PSA_OK;
+}
+
+psa_status psa_debug_issue_probe(int32_t pattern, int64_t* d_cycles, int64_t capacity, int32_t iters,
+                                 void* stream) {
+  if (!d_cycles) return set_error(PSA_ERR_INVALID_ARGUMENT, "cycles is NULL");
+  if (pattern < 0 || pattern > 7) return set_error(PSA_ERR_INVALID_ARGUMENT, "pattern must be 0..7");
+  if (iters <= 0) return set_error(PSA_ERR_INVALID_ARGUMENT, "iters must be positive");
+  const int blocks = 256;
+  if (capacity < (int64_t)blocks * 4)
+    return set_error(PSA_ERR_WORKSPACE_TOO_SMALL, "cycles needs " + std::to_string(blocks * 4) + " entries");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return psa::hip_fail(e, "hipGetDevice");
+  psa_status st = psa::check_device_ptr(d_cycles, "cycles", dev);
+  if (st != PSA_OK) return st;
+  e = psa::launch_issue_probe(pattern, d_cycles, iters, blocks, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return psa::hip_fail(e, "issue probe kernel launch");
   return PSA_OK;
 }
 

@@ -58,6 +58,120 @@ __global__ __launch_bounds__(kPeakThreads) void mfma_peak_kernel(float* out, int
   out[blockIdx.x * kPeakThreads + threadIdx.x] = c[0] + c[1] + c[2] + c[3];
 }
 
+// Issue-rate probe: each wave of one workgroup per CU (LDS padding leaves
+// room for no more), i.e. one wave per SIMD, times `iters` iterations of one
+// instruction pattern with s_memtime and lane 0 writes the cycles to
+// cycles[wave].  Patterns (per iteration):
+//   0..4: 16 v_mfma_f32_16x16x32_bf16 in 16, 8, 4, 2 or 1 independent
+//         accumulation chains;
+//   5:    16 independent v_fma_f32;
+//   6:    8 independent v_exp_f32;
+//   7:    16 MFMAs (8 chains) with 32 v_fma_f32 and 8 v_exp_f32 between them
+//         (two FMAs and half an exponential per MFMA: the softmax work the
+//         MFMA prefix tile issues per MFMA).
+// Values start opaque to the compiler (no common subexpressions) and every
+// result feeds a never-taken store, so nothing is removed.
+template <int P>
+__global__ __launch_bounds__(kPeakThreads, 1) void issue_probe_kernel(int64_t* cycles, int iters) {
+  __shared__ char pad[96 * 1024];
+  const int lane = threadIdx.x & 63;
+  bf16x8p a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(1e-3f * (float)((lane + i) & 7));
+    b[i] = (__bf16)(1e-3f * (float)((lane * 3 + i) & 7));
+  }
+  constexpr int NCH = P == 0 ? 16 : P == 1 ? 8 : P == 2 ? 4 : P == 3 ? 2 : P == 4 ? 1 : 8;
+  f32x4p acc[NCH];
+  float x[16], e[8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    acc[j] = f32x4p{1e-3f * (float)(lane + j), 0.f, 0.f, 0.f};
+    asm volatile("" : "+v"(acc[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    x[j] = 1e-3f * (float)(lane + j);
+    asm volatile("" : "+v"(x[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    e[j] = -1e-3f * (float)(lane + j);
+    asm volatile("" : "+v"(e[j]));
+  }
+  const float c1 = 0.999f, c0 = 1e-7f;
+  __syncthreads();
+  // the empty asm statements tie the values to the two clock reads, so the
+  // compiler moves no work out of the timed region
+  auto pin = [&]() {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(acc[j]));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(x[j]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(e[j]));
+  };
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  pin();
+  if constexpr (P <= 4) {
+    const int n = iters * (16 / NCH);
+    for (int it = 0; it < n; ++it) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else if constexpr (P == 5) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = fmaf(x[j], c1, c0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if constexpr (P == 6) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(e[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        acc[j % 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j % 8], 0, 0, 0);
+        x[j] = fmaf(x[j], c1, c0);
+        x[(j + 8) % 16] = fmaf(x[(j + 8) % 16], c1, c0);
+        if (j & 1) e[j / 2] = __builtin_amdgcn_exp2f(e[j / 2]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  pin();
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) sum += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sum += x[j];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += e[j];
+  const int w = blockIdx.x * (kPeakThreads / 64) + (threadIdx.x >> 6);
+  if (lane == 0) cycles[w] = (int64_t)(t1 - t0);
+  if (sum == 1.2345e-30f && pad[threadIdx.x] == 7) cycles[w] = -1;  // never: keeps every result live
+}
+
+hipError_t launch_issue_probe(int pattern, int64_t* cycles, int iters, int blocks, hipStream_t s) {
+  switch (pattern) {
+#define PSA_PROBE(P)                                                                                 \
+  case P:                                                                                            \
+    hipLaunchKernelGGL((issue_probe_kernel<P>), dim3(blocks), dim3(kPeakThreads), 0, s, cycles, iters); \
+    return hipGetLastError();
+    PSA_PROBE(0) PSA_PROBE(1) PSA_PROBE(2) PSA_PROBE(3) PSA_PROBE(4) PSA_PROBE(5) PSA_PROBE(6) PSA_PROBE(7)
+#undef PSA_PROBE
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_read_peak(const void* buf, uint32_t bytes, uint32_t* sink, int blocks, hipStream_t s) {
   hipLaunchKernelGGL(read_peak_kernel, dim3(blocks), dim3(kPeakThreads), 0, s, static_cast<const char*>(buf), bytes,
                      sink);

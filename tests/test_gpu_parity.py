@@ -590,6 +590,25 @@ def test_measured_peak_kernels_run():
 
 
 
+def test_issue_probe_runs():
+    """Every issue-probe pattern runs, writes a positive cycle count for every
+    wave, and the counts scale with the work (after a warm-up launch, four
+    times the iterations take more than three times the cycles)."""
+    import torch
+
+    cyc = torch.full((1024,), -1, dtype=torch.int64, device="cuda")
+    for pat in P.ISSUE_PATTERNS:
+        log(f"case issue probe pattern {pat}")
+        P.psa_debug_issue_probe(pat, cyc, 64)
+        P.psa_debug_issue_probe(pat, cyc, 64)
+        torch.cuda.synchronize()
+        short = cyc.clone()
+        P.psa_debug_issue_probe(pat, cyc, 256)
+        torch.cuda.synchronize()
+        assert bool((short > 0).all()) and bool((cyc > 0).all())
+        assert float(cyc.double().median()) > 3 * float(short.double().median())
+
+
 def test_workspace_must_hold_the_launching_plans_image():
     """A workspace overwritten by another plan's upload is refused before the
     launch; one overwritten outside the library (its image header no longer

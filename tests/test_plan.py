@@ -636,7 +636,7 @@ def test_family_tiles_edge_shapes(seed, r):
 
 
 def test_peak_entry_points_reject_bad_arguments():
-    """Argument checks of psa_debug_read_peak / psa_debug_mfma_peak come before
+    """Argument checks of psa_debug_read_peak / psa_debug_mfma_peak / psa_debug_issue_probe come before
     any device access (no GPU needed): NULL pointers, sizes out of range, and
     too-small sinks are errors with a message."""
     import ctypes as C
@@ -651,6 +651,10 @@ def test_peak_entry_points_reject_bad_arguments():
         (L.psa_debug_mfma_peak, (None, 2048 * 256, 64, None), "NULL"),
         (L.psa_debug_mfma_peak, (fake, 2048 * 256, 12, None), "multiple of 8"),
         (L.psa_debug_mfma_peak, (fake, 10, 64, None), "out needs"),
+        (L.psa_debug_issue_probe, (0, None, 1024, 16, None), "NULL"),
+        (L.psa_debug_issue_probe, (8, fake, 1024, 16, None), "pattern"),
+        (L.psa_debug_issue_probe, (0, fake, 1024, 0, None), "iters"),
+        (L.psa_debug_issue_probe, (0, fake, 1000, 16, None), "cycles needs"),
     ]
     for fn, args, msg in cases:
         assert fn(*args) != 0
