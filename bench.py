@@ -221,6 +221,59 @@ def trace_summary(P, plan, q, k, v, out, ws, flush, sink, info, path, wl, launch
         json.dump(res, f)
 
 
+def tiles_in_fused(P, plan, q, k, v, out, ws, flush, sink, info, wl, launches=3):
+    """MFMA utilisation of the prefix tiles inside the fused launch: traced
+    launches (psa_decode_attention_traced, caches flushed before each) give
+    each MFMA tile unit's start, end and CU; the tiles' algorithmic flops
+    (4 d per row and prefix token) over the time each CU is busy with tiles
+    (union of its tiles' intervals) at the CU's share of the dense bf16
+    peak.  Median over the launches."""
+    import numpy as np
+    import torch
+
+    units = int(info["num_items"])
+    it = np.asarray(plan.items()).reshape(units, 4, 8)
+    tile = (it[:, 0, 0] & 0xFF) == 2
+    flops_u = np.where(tile, 4.0 * wl.head_dim * it[:, 0, 7].astype(np.float64) * (it[:, 0, 4] - it[:, 0, 3]), 0.0)
+    per_cu_peak = BF16_MFMA_PEAK_TFLOPS * 1e12 / 256
+    fr, busy_l, cus_l, span_l = [], [], [], []
+    for _ in range(launches):
+        tr = torch.zeros(units * 4, dtype=torch.int64, device="cuda")
+        if flush is not None:
+            torch.sum(flush, dim=None, out=sink)
+        P.psa_decode_attention(plan, q, k, v, out, ws, trace=tr)
+        torch.cuda.synchronize()
+        t = tr.view(units, 4).cpu().numpy()
+        if not ((t[:, 0] > 0) & (t[:, 1] >= t[:, 0])).all():
+            continue
+        start, end = t[:, 0] / 100.0, t[:, 1] / 100.0  # 100 MHz clock -> us
+        cu = ((t[:, 2] >> 32) & 0xF) * 256 + ((t[:, 2] >> 8) & 0xFF)  # XCC, then SE / SH / CU of HW_ID
+        busy = 0.0
+        ids = np.unique(cu[tile])
+        for c in ids:  # union of the tile intervals on each CU
+            iv = sorted(zip(start[tile & (cu == c)], end[tile & (cu == c)]))
+            lo, hi = iv[0]
+            for a, b in iv[1:]:
+                if a > hi:
+                    busy += hi - lo
+                    lo, hi = a, b
+                else:
+                    hi = max(hi, b)
+            busy += hi - lo
+        fr.append(flops_u.sum() / (busy * 1e-6 * per_cu_peak))
+        busy_l.append(busy)
+        cus_l.append(len(ids))
+        span_l.append(float(end[tile].max() - start.min()))
+    if not fr:
+        return None
+    j = int(np.argsort(fr)[len(fr) // 2])
+    return {"mfma_frac_on_their_cus": fr[j], "tile_flops": float(flops_u.sum()), "cus": cus_l[j],
+            "cu_busy_us_sum": busy_l[j], "tiles_end_us": span_l[j], "launches": len(fr),
+            "note": "prefix tiles' flops (4 d x rows x chunk tokens of every tile; keys masked by a prefill row's "
+                    "causal limit included) over (time each CU runs tiles x the CU's 1/256 share of the 2.5 PFLOP/s "
+                    "dense bf16 peak), from traced fused launches; median launch"}
+
+
 def timed(fn, steps, flush, sink):
     """Mean ms of fn() over `steps` runs, HIP events around each run, caches
     flushed (by a read) before each."""
@@ -521,6 +574,7 @@ def run_one(args):
     if not args.no_components and args.flags == 0 and info["num_prefix_items"] > 0:
         rec["components"] = components(P, cfg, batch, wl, q, k, v, flush, sink, max(10, args.steps // 2), ms,
                                        rec.get("measured_peaks"))
+        rec["components"]["prefix_tiles_in_fused"] = tiles_in_fused(P, plan, q, k, v, out, ws, flush, sink, info, wl)
     if not args.no_identify and wl.name == "llama3_8b_8x100":
         rec["host_prefix_identification"] = host_identification(P)
     if not args.no_cpu_baseline:
