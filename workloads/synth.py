@@ -19,6 +19,8 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
+import re
+
 import numpy as np
 
 PAGE = 16
@@ -308,6 +310,13 @@ PRESETS = {
 
 
 def make_workload(name, seed=0):
+    """A preset by name; also "llama3_8b_<G>x100" for any group count G (the
+    8 x 100 shape with more or fewer prefix groups, for occupancy studies;
+    not part of PRESETS)."""
+    if name not in PRESETS:
+        m = re.fullmatch(r"llama3_8b_(\d+)x100", name)
+        if m and int(m.group(1)) > 0:
+            return build_single_level(name, 32, 8, 128, "bf16", [(2048, 100, (64, 512))] * int(m.group(1)), [], seed)
     return PRESETS[name](seed)
 
 
