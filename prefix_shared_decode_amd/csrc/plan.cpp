@@ -487,8 +487,10 @@ psa_status build_plan(const psa_config* cfg, const psa_batch* b, const psa_plan_
       for (auto& qq : q) {
         size_t np = 0;
         while (np < qq.size() && units[qq[np]].it[0].kind % 256 == ITEM_PREFIX_MFMA) ++np;
-        if (np > 2 * (size_t)kCusPerXcd && qq.size() > np) {
-          // More tiles than one round of pairs.  Tiles whose prefix chunk
+        if (np > 2 * (size_t)kCusPerXcd - 8 && qq.size() > np) {
+          // Pairs would leave fewer than 4 of the XCD's CUs to the mat-vec
+          // units at the start (16 groups of 8x100, 64 tiles an XCD: 0.392
+          // ms spread, 0.407 in pairs).  Tiles whose prefix chunk
           // has several row tiles read it from L2 and are bound by their
           // compute: spread evenly over the first 3/4 of the queue, they run
           // beside the HBM-bound mat-vec units instead of in a phase of

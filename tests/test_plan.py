@@ -516,6 +516,30 @@ def test_mfma_tiles_beyond_a_round_of_pairs():
         _check_coverage(fw, plan)
 
 
+def test_tile_pairs_leave_mat_vec_room_at_the_start():
+    """Pairs are kept while they leave at least 4 of an XCD's 32 CUs to the
+    mat-vec units when the launch starts: 14 groups of the 8x100 shape (56
+    tiles an XCD, 28 CUs of pairs) keep pairs at [0, 28) and [32, 60); 15
+    groups (60 tiles, 2 CUs left) are spread like the compute-bound tiles
+    of the mixed preset."""
+    from workloads import make_workload
+
+    for g, paired in ((14, True), (15, False)):
+        wl = make_workload(f"llama3_8b_{g}x100")
+        plan = P.psa_build_plan(_cfg(wl), wl.batch)
+        kinds = plan.items()[::4, 0] & 0xFF
+        for x in range(8):
+            pos = np.nonzero(kinds[x::8] == 2)[0]
+            assert len(pos) == 4 * g, (g, x)
+            if paired:
+                assert list(pos) == list(range(28)) + list(range(32, 60)), x
+            else:
+                span = int(0.75 * len(kinds[x::8]))
+                want = np.ceil(np.arange(len(pos)) * span / len(pos))
+                assert np.abs(pos - want).max() <= 1, x
+        _check_coverage(wl, plan)
+
+
 def _flat(wl):
     batch, _ = P.psa_flatten_prefix_tree(wl.tree)
 
