@@ -497,7 +497,10 @@ def test_merge_paths_give_the_same_bits(case):
 
 # ---------------- full-size workloads, whole output ----------------
 
-FULL = ["llama3_8b_8x100", "longchat13b_1x256", "no_sharing_512", "two_level_4x16x16", "mixed_7prefill_256decode"]
+FULL = ["llama3_8b_8x100", "longchat13b_1x256", "no_sharing_512", "two_level_4x16x16", "mixed_7prefill_256decode",
+        # the 8x100 shape with 15 groups: 60 MFMA tiles an XCD, spread through
+        # the queue between the mat-vec units instead of paired at its start
+        "llama3_8b_15x100"]
 # queries per oracle worker batch (the LongChat-like contexts are 10.8K tokens x 40 heads)
 FULL_CHUNK = {"longchat13b_1x256": 4}
 
